@@ -1,0 +1,139 @@
+"""C ABI checks that need no GPU: exported symbols and fail-closed host validation.
+
+Validation happens before any launch ("fail closed on malformed layouts ... and invalid route
+maps", 'serve canonical Fruit QSRT atoms' (b12x PR #129), Summary; a short or misaligned arena is
+rejected, 'TrellisMX (procedural NPK) ... P8 runtime' (flashinfer PR #69), description), so every
+call below returns before touching a (fake) device pointer."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "tmoe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tmoe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def N():
+    from trellis_quantized_moe_tmoe_amd import native
+    return native
+
+
+def test_library_exports_every_declared_symbol(N):
+    declared = _declared_symbols()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(N.lib, name), name
+    assert sorted(N.EXPORTS) == declared
+
+
+def _cfg(N, bits, **kw):
+    d = dict(hidden=1024, inter=512, num_experts=len(bits), top_k=8, max_tokens=16, rotation=0, ids_dtype=1,
+             block_m=0)
+    d.update(kw)
+    arr = (ctypes.c_uint8 * len(bits))(*bits)
+    c = N.Config(d["hidden"], d["inter"], d["num_experts"], d["top_k"], d["max_tokens"],
+                 ctypes.cast(arr, ctypes.POINTER(ctypes.c_uint8)), d["rotation"], d["ids_dtype"], d["block_m"])
+    return c, arr
+
+
+def _plan(N, bits, **kw):
+    c, keep = _cfg(N, bits, **kw)
+    h = ctypes.c_void_p()
+    sb, pw = ctypes.c_size_t(), ctypes.c_size_t()
+    st = N.lib.tmoe_plan(ctypes.byref(c), ctypes.byref(h), ctypes.byref(sb), ctypes.byref(pw))
+    return st, h, sb.value, pw.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=1000), 2), (dict(inter=96), 2), (dict(hidden=8192), 2), (dict(hidden=0), 1),
+    (dict(top_k=0), 1), (dict(top_k=33), 2), (dict(max_tokens=0), 1), (dict(rotation=2), 1),
+    (dict(ids_dtype=3), 1), (dict(block_m=24), 1), (dict(block_m=48), 0), (dict(hidden=2560, inter=320), 0),
+])
+def test_plan_validation(N, kw, status):
+    st, h, _, _ = _plan(N, [4] * 8, **kw)
+    assert st == status
+    if st == 0:
+        assert N.lib.tmoe_plan_destroy(h) == 0
+
+
+@pytest.mark.parametrize("bits,status", [([4, 3, 2], 0), ([4, 5], 2), ([1], 2), ([0], 1), ([17], 1)])
+def test_plan_bit_widths(N, bits, status):
+    assert _plan(N, bits)[0] == status
+
+
+def test_plan_too_many_experts(N):
+    assert _plan(N, [4] * 513)[0] == 2
+
+
+def test_payload_words_and_offsets(N):
+    bits = [4, 3, 2, 4]
+    st, h, sb, pw = _plan(N, bits, hidden=2560, inter=320)
+    assert st == 0
+    per_bit = 3 * 2560 * 320 // 16
+    assert pw == per_bit * sum(bits)
+    off = ctypes.c_size_t()
+    for e, want in enumerate(np.concatenate([[0], np.cumsum(bits)[:-1]]) * per_bit):
+        assert N.lib.tmoe_plan_expert_offset(h, e, ctypes.byref(off)) == 0 and off.value == want
+    assert N.lib.tmoe_plan_expert_offset(h, 4, ctypes.byref(off)) == 1
+    info = N.PlanInfo()
+    assert N.lib.tmoe_plan_get_info(h, ctypes.byref(info)) == 0 and info.scratch_bytes == sb
+    N.lib.tmoe_plan_destroy(h)
+
+
+def test_forward_fails_closed_before_any_launch(N):
+    st, h, sb, _ = _plan(N, [4] * 8)
+    fake = 1 << 20                                # never dereferenced: validation returns first
+    w = N.Weights(*([fake] * 7))
+    fw = N.lib.tmoe_forward_w4a16
+    args = lambda **o: [h, o.get("x", fake), o.get("ids", fake), o.get("w", fake), o.get("T", 4),
+                        ctypes.byref(o.get("wt", w)), o.get("y", fake), o.get("scratch", fake),
+                        o.get("bytes", sb), None]
+    assert fw(*args(T=17)) == 4                   # above capacity
+    assert fw(*args(T=-1)) == 1
+    assert fw(*args(T=0)) == 0                    # nothing to do, nothing launched
+    assert fw(*args(bytes=sb - 1)) == 3           # short arena
+    assert fw(*args(scratch=fake + 8)) == 3       # arena not 16-byte aligned
+    assert fw(*args(scratch=0)) == 3
+    assert fw(*args(ids=0)) == 1
+    assert fw(*args(ids=fake + 4)) == 5           # int64 ids need 8-byte alignment
+    assert fw(*args(x=0)) == 1
+    assert fw(*args(y=fake + 4)) == 5
+    assert fw(*args(wt=N.Weights(*([fake] * 6 + [0])))) == 1
+    assert N.lib.tmoe_forward_w4a8(*args(T=17)) == 4
+    N.lib.tmoe_plan_destroy(h)
+
+
+def test_w4a8_needs_128_multiples(N):
+    st, h, sb, _ = _plan(N, [4] * 8, hidden=2560, inter=320)
+    fake = 1 << 20
+    w = N.Weights(*([fake] * 7))
+    assert N.lib.tmoe_forward_w4a8(h, fake, fake, fake, 2, ctypes.byref(w), fake, fake, sb, None) == 2
+    N.lib.tmoe_plan_destroy(h)
+
+
+def test_route_map_and_debug_validation(N):
+    st, h, sb, _ = _plan(N, [4] * 8)
+    view = N.RouteMap()
+    fake = 1 << 20
+    assert N.lib.tmoe_build_route_map(h, fake, 17, fake, sb, ctypes.byref(view), None) == 4
+    assert N.lib.tmoe_build_route_map(h, fake, 2, fake, sb - 16, ctypes.byref(view), None) == 3
+    assert N.lib.tmoe_build_route_map(h, fake, 2, fake, sb, None, None) == 1
+    w = N.Weights(*([fake] * 7))
+    assert N.lib.tmoe_debug_decode(h, ctypes.byref(w), 8, 0, 0, fake, None) == 1
+    assert N.lib.tmoe_debug_decode(h, ctypes.byref(w), 0, 2, 0, fake, None) == 1
+    assert N.lib.tmoe_debug_mxfp8(fake, 4, 48, fake, fake, None) == 1
+    assert N.lib.tmoe_debug_rotate(fake, 4, 100, None) == 2
+    v = N.DebugViews()
+    assert N.lib.tmoe_debug_get_views(h, 17, 0, fake, sb, ctypes.byref(v)) == 4
+    assert N.lib.tmoe_debug_get_views(h, 4, 0, fake, sb, ctypes.byref(v)) == 0
+    assert v.splits1 >= 1 and v.splits2 >= 1
+    assert N.lib.tmoe_status_str(3).decode().startswith("scratch")
+    N.lib.tmoe_plan_destroy(h)

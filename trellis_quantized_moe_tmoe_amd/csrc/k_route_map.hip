@@ -1,0 +1,179 @@
+// k_route_map.hip -- stable token-major route map in one workgroup.
+//
+// The route map is materialised once and consumed directly by FC1 and FC2 ("serve canonical Fruit
+// QSRT atoms", Hot path); per-expert counts and an exclusive prefix give expert offsets and routed
+// blocks (sparkinfer PR #90, review of route_pack.py). Stable token-major order within an expert
+// follows the O(routes + experts * tiles) stable design asked for in the review of route_pack.py
+// on "Share trellis preparation across native and EXL3 containers": the routes are walked once per
+// pass in wave-sized chunks, and per-wave, per-expert running positions replace any rescan.
+//
+// Same-expert lanes of a 64-route chunk are found with one ballot per key bit (a "multi-split"):
+// the AND of the ballots that agree with a lane's key bits is exactly the set of lanes holding the
+// same key, so the rank of a lane among equal keys is a popcount. That costs ceil(log2(E+1))
+// ballots per chunk, independent of how many distinct experts the chunk holds.
+#include "tmoe_device.hpp"
+#include "tmoe_internal.hpp"
+
+namespace tmoe {
+
+namespace {
+
+constexpr int kWaves = 16;           // 1024 threads
+constexpr int kMaxExperts = 512;
+
+// Exclusive scan over the workgroup (one value per thread); total returned in *total.
+__device__ int block_exclusive_scan(int v, int* smem, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) smem[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < kWaves ? smem[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < kWaves; d <<= 1) {
+      const int y = __shfl_up(s, d, 64);
+      if (lane >= d) s += y;
+    }
+    if (lane < kWaves) smem[lane] = s;
+  }
+  __syncthreads();
+  const int prefix = w > 0 ? smem[w - 1] : 0;
+  *total = smem[kWaves - 1];
+  __syncthreads();
+  return prefix + x - v;
+}
+
+__device__ __forceinline__ long long load_id(const void* ids, int ids64, int r) {
+  return ids64 ? static_cast<const long long*>(ids)[r] : static_cast<long long>(static_cast<const int*>(ids)[r]);
+}
+
+// Lanes of the current chunk that hold the same key as this lane (among `active` lanes).
+__device__ __forceinline__ unsigned long long same_key_mask(int key, int nbits, unsigned long long active) {
+  unsigned long long m = active;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const unsigned long long bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return m;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
+  __shared__ int cnt[kWaves * kMaxExperts];   // per wave, per expert: count, then running slot
+  __shared__ int scan_smem[kWaves];
+  __shared__ int bad_w[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int E = a.num_experts, R = a.routes;
+  for (int i = tid; i < kWaves * E; i += 1024) cnt[i] = 0;
+  if (tid < kWaves) bad_w[tid] = 0;
+  __syncthreads();
+
+  const int nbits = 32 - __clz(E);              // keys 0..E (E marks an invalid id)
+  const int seg = (R + kWaves - 1) / kWaves;
+  const int beg = w * seg, end = min(R, beg + seg);
+  const unsigned long long lt = (1ull << lane) - 1ull;
+
+  // pass 1: per-wave per-expert counts
+  for (int base = beg; base < end; base += 64) {
+    const int r = base + lane;
+    const bool act = r < end;
+    const long long id = act ? load_id(a.ids, a.ids64, r) : -1;
+    const bool valid = act && id >= 0 && id < E;
+    const int key = valid ? static_cast<int>(id) : E;
+    const unsigned long long active = __ballot(act);
+    const unsigned long long m = same_key_mask(key, nbits, active);
+    const bool leader = act && ((m >> lane) == 1ull);        // highest lane of its key group
+    if (leader) {
+      const int c = __popcll(m);
+      if (valid) cnt[w * E + key] += c;
+      else bad_w[w] += c;
+    }
+  }
+  __syncthreads();
+
+  // expert totals, offsets, and per-wave starting slots; tile counts for both tile tables
+  int total_e = 0, bits_e = 0;
+  const bool own = tid < E;                      // E <= 512 < 1024: one expert per thread
+  if (own) {
+    for (int ww = 0; ww < kWaves; ++ww) total_e += cnt[ww * E + tid];
+    bits_e = static_cast<int>((a.packed_bits[tid >> 4] >> (2 * (tid & 15))) & 3u) + 2;
+  }
+  int n_valid = 0, n_tiles = 0, n_gtiles = 0, bit_units = 0;
+  const int tiles_e = own ? (total_e + a.block_m - 1) / a.block_m : 0;
+  const int gtiles_e = own ? (total_e + a.gemm_rows - 1) / a.gemm_rows : 0;
+  const int off_e = block_exclusive_scan(own ? total_e : 0, scan_smem, &n_valid);
+  const int toff_e = block_exclusive_scan(tiles_e, scan_smem, &n_tiles);
+  const int goff_e = block_exclusive_scan(gtiles_e, scan_smem, &n_gtiles);
+  const int boff_e = block_exclusive_scan(own ? bits_e : 0, scan_smem, &bit_units);
+  if (own) {
+    int acc = off_e;
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const int c = cnt[ww * E + tid];
+      cnt[ww * E + tid] = acc;
+      acc += c;
+    }
+    a.counts[tid] = total_e;
+    a.offsets[tid] = off_e;
+    ExpertInfo info;
+    info.word_offset = static_cast<long long>(boff_e) * a.words_per_bit;
+    info.bits = bits_e;
+    info.pad = 0;
+    a.einfo[tid] = info;
+    for (int t = 0; t < tiles_e; ++t) {
+      a.tile_expert[toff_e + t] = tid;
+      a.tile_row0[toff_e + t] = off_e + t * a.block_m;
+      a.tile_rows[toff_e + t] = min(a.block_m, total_e - t * a.block_m);
+    }
+    for (int t = 0; t < gtiles_e; ++t) {
+      int4 g;
+      g.x = tid;
+      g.y = off_e + t * a.gemm_rows;
+      g.z = min(a.gemm_rows, total_e - t * a.gemm_rows);
+      g.w = 0;
+      a.gtiles[goff_e + t] = g;
+    }
+  }
+  if (tid == 0) {
+    a.offsets[E] = n_valid;
+    *a.num_tiles = n_tiles;
+    *a.num_gtiles = n_gtiles;
+    int bad = 0;
+    for (int ww = 0; ww < kWaves; ++ww) bad += bad_w[ww];
+    *a.status = bad;
+  }
+  __syncthreads();
+
+  // pass 2: stable placement, chunk by chunk in route order within each wave's segment
+  for (int base = beg; base < end; base += 64) {
+    const int r = base + lane;
+    const bool act = r < end;
+    const long long id = act ? load_id(a.ids, a.ids64, r) : -1;
+    const bool valid = act && id >= 0 && id < E;
+    const int key = valid ? static_cast<int>(id) : E;
+    const unsigned long long active = __ballot(act);
+    const unsigned long long m = same_key_mask(key, nbits, active);
+    if (valid) {
+      const int pos = cnt[w * E + key] + __popcll(m & lt);
+      a.sorted_routes[pos] = r;
+      a.route_slot[r] = pos;
+    } else if (act) {
+      a.route_slot[r] = -1;
+    }
+    // every lane of the wave has read its running slot above (LDS accesses of one wave complete
+    // in order), so the group leader may now advance it
+    if (valid && ((m >> lane) == 1ull)) cnt[w * E + key] += __popcll(m);
+  }
+}
+
+void launch_route_map(const RouteMapArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_route_map, dim3(1), dim3(1024), 0, s, a);
+}
+
+}  // namespace tmoe

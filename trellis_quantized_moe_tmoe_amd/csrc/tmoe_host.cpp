@@ -1,0 +1,454 @@
+// tmoe_host.cpp -- the C ABI: plan validation, scratch layout and the launch sequence.
+//
+// Every argument is checked before the first launch, so a rejected call leaves the caller's
+// output and scratch untouched ("fail closed on malformed layouts ... and invalid route maps",
+// "serve canonical Fruit QSRT atoms", Summary). Plans are host-only; the library allocates
+// nothing: per-expert payload offsets travel as packed launch arguments and are expanded into the
+// caller's scratch by the route-map kernel, so a forward call can be captured into a hipGraph.
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/tmoe.h"
+#include "tmoe_device.hpp"
+#include "tmoe_internal.hpp"
+
+using namespace tmoe;
+
+namespace {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxDim = 4096;
+constexpr long long kMaxRoutes = 1LL << 24;
+constexpr size_t kAlign = 256;
+constexpr int kGemmWaveCap = 4096;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
+
+RowRot make_rot(int n, int identity) {
+  RowRot r;
+  r.n = n;
+  r.pow2 = is_pow2(n) ? 1 : 0;
+  r.nblk128 = r.pow2 ? 0 : n / 128;
+  r.tail64 = r.pow2 ? 0 : ((n % 128) ? 1 : 0);
+  r.identity = identity;
+  return r;
+}
+
+// K-split count: more splits for fewer routes so small batches still fill the chip; must divide
+// the K steps so every split has the same depth.
+int choose_splits(long long routes, int ksteps) {
+  int target = routes <= 32 ? 8 : routes <= 128 ? 4 : routes <= 512 ? 2 : 1;
+  for (int s = target; s > 1; s >>= 1)
+    if (ksteps % s == 0) return s;
+  return 1;
+}
+
+int choose_mg(long long routes, int experts) {
+  if (routes <= 2LL * experts) return 1;
+  if (routes <= 8LL * experts) return 2;
+  return 4;
+}
+
+struct Layout {
+  size_t einfo, counts, offsets, sorted, slot, tile_e, tile_r0, tile_rows, scalars, gtiles;
+  size_t a1, z, b, v, total;
+};
+
+}  // namespace
+
+struct tmoe_plan_s {
+  int H, I, E, K, max_tokens, rotation, ids64, block_m;
+  std::vector<uint8_t> bits;
+  std::vector<long long> offsets;   // word offset per expert, [E+1]
+  uint32_t packed_bits[32];
+  long long routes_max;
+  int max_tiles, max_gtiles;
+  bool fp8_ok;
+  Layout lay;
+};
+
+namespace {
+
+long long max_split_rows(long long rmax, int ksteps_a, int ksteps_b) {
+  long long best = rmax;
+  const long long pts[4] = {std::min(rmax, 32LL), std::min(rmax, 128LL), std::min(rmax, 512LL), rmax};
+  for (long long r : pts)
+    for (int ks : {ksteps_a, ksteps_b}) best = std::max(best, r * choose_splits(r, ks));
+  return best;
+}
+
+void build_layout(tmoe_plan_s* p) {
+  const long long R = p->routes_max;
+  Layout& L = p->lay;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  L.einfo = take(sizeof(ExpertInfo) * p->E);
+  L.counts = take(4ull * p->E);
+  L.offsets = take(4ull * (p->E + 1));
+  L.sorted = take(4ull * R);
+  L.slot = take(4ull * R);
+  L.tile_e = take(4ull * p->max_tiles);
+  L.tile_r0 = take(4ull * p->max_tiles);
+  L.tile_rows = take(4ull * p->max_tiles);
+  L.scalars = take(16);                               // num_tiles, status, num_gtiles
+  L.gtiles = take(16ull * p->max_gtiles);
+  L.a1 = take(2ull * R * p->H);                       // fp16, or E4M3 + E8M0 planes
+  const long long zrows = max_split_rows(R, p->H / 32, p->H / 128 > 0 ? p->H / 128 : 1);
+  L.z = take(4ull * zrows * 2 * p->I);
+  L.b = take(2ull * R * p->I);
+  const long long vrows = max_split_rows(R, p->I / 32, p->I / 128 > 0 ? p->I / 128 : 1);
+  L.v = take(4ull * vrows * p->H);
+  L.total = off;
+}
+
+template <class T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+tmoe_status check_scratch(const tmoe_plan_s* p, void* scratch, size_t bytes) {
+  if (!scratch) return TMOE_ERR_SCRATCH;
+  if (!aligned(scratch, 16)) return TMOE_ERR_SCRATCH;
+  if (bytes < p->lay.total) return TMOE_ERR_SCRATCH;
+  return TMOE_OK;
+}
+
+tmoe_route_map make_view(const tmoe_plan_s* p, void* scratch) {
+  tmoe_route_map v;
+  v.counts = at<int32_t>(scratch, p->lay.counts);
+  v.offsets = at<int32_t>(scratch, p->lay.offsets);
+  v.sorted_routes = at<int32_t>(scratch, p->lay.sorted);
+  v.route_slot = at<int32_t>(scratch, p->lay.slot);
+  v.tile_expert = at<int32_t>(scratch, p->lay.tile_e);
+  v.tile_row0 = at<int32_t>(scratch, p->lay.tile_r0);
+  v.tile_rows = at<int32_t>(scratch, p->lay.tile_rows);
+  v.num_tiles = at<int32_t>(scratch, p->lay.scalars);
+  v.status = at<int32_t>(scratch, p->lay.scalars) + 1;
+  v.max_tiles = p->max_tiles;
+  v.block_m = p->block_m;
+  return v;
+}
+
+void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_rows, void* scratch,
+                       hipStream_t st) {
+  RouteMapArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.ids = ids;
+  a.ids64 = p->ids64;
+  a.routes = T * p->K;
+  a.num_experts = p->E;
+  a.block_m = p->block_m;
+  a.gemm_rows = gemm_rows;
+  a.words_per_bit = 3LL * p->H * p->I / 16;
+  a.counts = at<int32_t>(scratch, p->lay.counts);
+  a.offsets = at<int32_t>(scratch, p->lay.offsets);
+  a.sorted_routes = at<int32_t>(scratch, p->lay.sorted);
+  a.route_slot = at<int32_t>(scratch, p->lay.slot);
+  a.tile_expert = at<int32_t>(scratch, p->lay.tile_e);
+  a.tile_row0 = at<int32_t>(scratch, p->lay.tile_r0);
+  a.tile_rows = at<int32_t>(scratch, p->lay.tile_rows);
+  a.num_tiles = at<int32_t>(scratch, p->lay.scalars);
+  a.status = at<int32_t>(scratch, p->lay.scalars) + 1;
+  a.num_gtiles = at<int32_t>(scratch, p->lay.scalars) + 2;
+  a.gtiles = at<int4>(scratch, p->lay.gtiles);
+  a.einfo = at<ExpertInfo>(scratch, p->lay.einfo);
+  std::memcpy(a.packed_bits, p->packed_bits, sizeof(a.packed_bits));
+  launch_route_map(a, st);
+}
+
+tmoe_status check_common(const tmoe_plan_s* p, const void* ids, int T, void* scratch, size_t bytes) {
+  if (!p) return TMOE_ERR_INVALID_ARG;
+  if (T < 0) return TMOE_ERR_INVALID_ARG;
+  if (T > p->max_tokens) return TMOE_ERR_CAPACITY;
+  if (T == 0) return TMOE_OK;
+  if (!ids) return TMOE_ERR_INVALID_ARG;
+  if (!aligned(ids, p->ids64 ? 8 : 4)) return TMOE_ERR_ALIGNMENT;
+  return check_scratch(p, scratch, bytes);
+}
+
+tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* w, int32_t T,
+                    const tmoe_weights* wt, float* y, void* scratch, size_t bytes, void* stream, bool fp8) {
+  tmoe_status st = check_common(p, ids, T, scratch, bytes);
+  if (st != TMOE_OK) return st;
+  if (fp8 && !p->fp8_ok) return TMOE_ERR_UNSUPPORTED;
+  if (T == 0) return TMOE_OK;
+  if (!x || !w || !wt || !y) return TMOE_ERR_INVALID_ARG;
+  if (!wt->payload || !wt->scale1 || !wt->scale2 || !wt->su1 || !wt->sv1 || !wt->su2 || !wt->sv2)
+    return TMOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 4) || !aligned(wt->payload, 16) ||
+      !aligned(wt->scale1, 2) || !aligned(wt->scale2, 2) || !aligned(wt->su1, 2) || !aligned(wt->sv1, 2) ||
+      !aligned(wt->su2, 2) || !aligned(wt->sv2, 2))
+    return TMOE_ERR_ALIGNMENT;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long long R = static_cast<long long>(T) * p->K;
+  const int mg = choose_mg(R, p->E);
+  const int gemm_rows = 16 * mg;
+  const int kdiv = fp8 ? 128 : 32;
+  const int s1 = choose_splits(R, p->H / kdiv);
+  const int s2 = choose_splits(R, p->I / kdiv);
+  const long long gt_ub = std::min<long long>(R, p->E + R / gemm_rows + 1);
+
+  (void)hipGetLastError();   // clear a stale error so the check below reports this call only
+  enqueue_route_map(p, ids, T, gemm_rows, scratch, s);
+
+  const int32_t* sorted = at<int32_t>(scratch, p->lay.sorted);
+  const int32_t* offsets = at<int32_t>(scratch, p->lay.offsets);
+  uint8_t* a1 = at<uint8_t>(scratch, p->lay.a1);
+  uint8_t* a1s = a1 + static_cast<size_t>(R) * p->H;
+  uint8_t* bq = at<uint8_t>(scratch, p->lay.b);
+  uint8_t* bs = bq + static_cast<size_t>(R) * p->I;
+  float* z = at<float>(scratch, p->lay.z);
+  float* v = at<float>(scratch, p->lay.v);
+
+  RotateArgs ra;
+  ra.x = static_cast<const uint16_t*>(x);
+  ra.ids = ids;
+  ra.ids64 = p->ids64;
+  ra.top_k = p->K;
+  ra.sorted_routes = sorted;
+  ra.offsets = offsets;
+  ra.num_experts = p->E;
+  ra.su1 = wt->su1;
+  ra.rot = make_rot(p->H, p->rotation == TMOE_ROT_IDENTITY);
+  ra.a1 = a1;
+  ra.a1_scale = a1s;
+  ra.routes = static_cast<int>(R);
+  launch_rotate(ra, fp8, s);
+
+  GemmArgs g1;
+  g1.payload = wt->payload;
+  g1.einfo = at<ExpertInfo>(scratch, p->lay.einfo);
+  g1.fc2_words_per_bit = 0;
+  g1.a = a1;
+  g1.a_scale = a1s;
+  g1.out = z;
+  g1.gtiles = at<int4>(scratch, p->lay.gtiles);
+  g1.num_gtiles = at<int32_t>(scratch, p->lay.scalars) + 2;
+  g1.K = p->H;
+  g1.N = 2 * p->I;
+  g1.splits = s1;
+  g1.routes = static_cast<int>(R);
+  const int waves1 = static_cast<int>(std::min<long long>(kGemmWaveCap, gt_ub * (g1.N / 64) * s1));
+  if (fp8) launch_gemm_f8(g1, mg, waves1, s);
+  else launch_gemm_f16(g1, mg, waves1, s);
+
+  ActArgs aa;
+  aa.z = z;
+  aa.splits = s1;
+  aa.ids = ids;
+  aa.ids64 = p->ids64;
+  aa.sorted_routes = sorted;
+  aa.offsets = offsets;
+  aa.num_experts = p->E;
+  aa.scale1 = wt->scale1;
+  aa.sv1 = wt->sv1;
+  aa.su2 = wt->su2;
+  aa.rot = make_rot(p->I, p->rotation == TMOE_ROT_IDENTITY);
+  aa.b = bq;
+  aa.b_scale = bs;
+  aa.routes = static_cast<int>(R);
+  launch_act(aa, fp8, s);
+
+  GemmArgs g2 = g1;
+  g2.fc2_words_per_bit = 2LL * p->H * p->I / 16;
+  g2.a = bq;
+  g2.a_scale = bs;
+  g2.out = v;
+  g2.K = p->I;
+  g2.N = p->H;
+  g2.splits = s2;
+  const int waves2 = static_cast<int>(std::min<long long>(kGemmWaveCap, gt_ub * (g2.N / 64) * s2));
+  if (fp8) launch_gemm_f8(g2, mg, waves2, s);
+  else launch_gemm_f16(g2, mg, waves2, s);
+
+  CombineArgs ca;
+  ca.v = v;
+  ca.splits = s2;
+  ca.ids = ids;
+  ca.ids64 = p->ids64;
+  ca.w = w;
+  ca.route_slot = at<int32_t>(scratch, p->lay.slot);
+  ca.top_k = p->K;
+  ca.tokens = T;
+  ca.routes = static_cast<int>(R);
+  ca.scale2 = wt->scale2;
+  ca.sv2 = wt->sv2;
+  ca.rot = make_rot(p->H, p->rotation == TMOE_ROT_IDENTITY);
+  ca.y = y;
+  launch_combine(ca, s);
+
+  return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
+}
+
+bool dim_ok(int n) { return n >= 64 && n <= kMaxDim && n % 64 == 0; }
+
+}  // namespace
+
+extern "C" {
+
+tmoe_status tmoe_plan(const tmoe_config* cfg, tmoe_plan_t* out, size_t* scratch_bytes, size_t* payload_words) {
+  if (!cfg || !out) return TMOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (cfg->hidden <= 0 || cfg->inter <= 0 || cfg->num_experts <= 0 || cfg->top_k <= 0 || cfg->max_tokens <= 0)
+    return TMOE_ERR_INVALID_ARG;
+  if (!cfg->expert_bits) return TMOE_ERR_INVALID_ARG;
+  if (cfg->rotation != TMOE_ROT_HADAMARD && cfg->rotation != TMOE_ROT_IDENTITY) return TMOE_ERR_INVALID_ARG;
+  if (cfg->ids_dtype != TMOE_IDS_I32 && cfg->ids_dtype != TMOE_IDS_I64) return TMOE_ERR_INVALID_ARG;
+  const int bm = cfg->block_m;
+  if (bm != 0 && bm != 8 && bm != 16 && bm != 32 && bm != 48 && bm != 64) return TMOE_ERR_INVALID_ARG;
+  if (!dim_ok(cfg->hidden) || !dim_ok(cfg->inter)) return TMOE_ERR_UNSUPPORTED;
+  if (cfg->num_experts > kMaxExperts || cfg->top_k > kMaxTopK) return TMOE_ERR_UNSUPPORTED;
+  const long long rmax = static_cast<long long>(cfg->max_tokens) * cfg->top_k;
+  if (rmax > kMaxRoutes) return TMOE_ERR_UNSUPPORTED;
+  for (int e = 0; e < cfg->num_experts; ++e) {
+    const int b = cfg->expert_bits[e];
+    if (b < 1 || b > 16) return TMOE_ERR_INVALID_ARG;
+    if (b < 2 || b > 4) return TMOE_ERR_UNSUPPORTED;
+  }
+  tmoe_plan_s* p = new (std::nothrow) tmoe_plan_s();
+  if (!p) return TMOE_ERR_INVALID_ARG;
+  p->H = cfg->hidden;
+  p->I = cfg->inter;
+  p->E = cfg->num_experts;
+  p->K = cfg->top_k;
+  p->max_tokens = cfg->max_tokens;
+  p->rotation = cfg->rotation;
+  p->ids64 = cfg->ids_dtype == TMOE_IDS_I64;
+  p->block_m = bm ? bm : 16;
+  p->bits.assign(cfg->expert_bits, cfg->expert_bits + p->E);
+  p->offsets.assign(p->E + 1, 0);
+  std::memset(p->packed_bits, 0, sizeof(p->packed_bits));
+  for (int e = 0; e < p->E; ++e) {
+    p->offsets[e + 1] = p->offsets[e] + 3LL * p->H * p->I * p->bits[e] / 16;
+    p->packed_bits[e >> 4] |= static_cast<uint32_t>(p->bits[e] - 2) << (2 * (e & 15));
+  }
+  p->routes_max = rmax;
+  p->max_tiles = static_cast<int>(rmax / p->block_m + p->E + 1);
+  p->max_gtiles = static_cast<int>(rmax / 16 + p->E + 1);
+  p->fp8_ok = (p->H % 128 == 0) && (p->I % 128 == 0);
+  build_layout(p);
+  *out = p;
+  if (scratch_bytes) *scratch_bytes = p->lay.total;
+  if (payload_words) *payload_words = static_cast<size_t>(p->offsets[p->E]);
+  return TMOE_OK;
+}
+
+tmoe_status tmoe_plan_destroy(tmoe_plan_t plan) {
+  if (!plan) return TMOE_ERR_INVALID_ARG;
+  delete plan;
+  return TMOE_OK;
+}
+
+tmoe_status tmoe_plan_get_info(tmoe_plan_t p, tmoe_plan_info* info) {
+  if (!p || !info) return TMOE_ERR_INVALID_ARG;
+  info->scratch_bytes = p->lay.total;
+  info->payload_words = static_cast<size_t>(p->offsets[p->E]);
+  info->block_m = p->block_m;
+  info->max_tiles = p->max_tiles;
+  return TMOE_OK;
+}
+
+tmoe_status tmoe_plan_expert_offset(tmoe_plan_t p, int32_t expert, size_t* word_offset) {
+  if (!p || !word_offset || expert < 0 || expert >= p->E) return TMOE_ERR_INVALID_ARG;
+  *word_offset = static_cast<size_t>(p->offsets[expert]);
+  return TMOE_OK;
+}
+
+tmoe_status tmoe_build_route_map(tmoe_plan_t p, const void* ids, int32_t T, void* scratch, size_t bytes,
+                                 tmoe_route_map* view, void* stream) {
+  tmoe_status st = check_common(p, ids, T, scratch, bytes);
+  if (st != TMOE_OK) return st;
+  if (!view) return TMOE_ERR_INVALID_ARG;
+  if (T == 0) return TMOE_OK;
+  const long long R = static_cast<long long>(T) * p->K;
+  (void)hipGetLastError();
+  enqueue_route_map(p, ids, T, 16 * choose_mg(R, p->E), scratch, static_cast<hipStream_t>(stream));
+  *view = make_view(p, scratch);
+  return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
+}
+
+tmoe_status tmoe_forward_w4a16(tmoe_plan_t p, const void* x, const void* ids, const float* w, int32_t T,
+                               const tmoe_weights* wt, float* y, void* scratch, size_t bytes, void* stream) {
+  return forward(p, x, ids, w, T, wt, y, scratch, bytes, stream, false);
+}
+
+tmoe_status tmoe_forward_w4a8(tmoe_plan_t p, const void* x, const void* ids, const float* w, int32_t T,
+                              const tmoe_weights* wt, float* y, void* scratch, size_t bytes, void* stream) {
+  return forward(p, x, ids, w, T, wt, y, scratch, bytes, stream, true);
+}
+
+const char* tmoe_status_str(tmoe_status s) {
+  switch (s) {
+    case TMOE_OK: return "ok";
+    case TMOE_ERR_INVALID_ARG: return "invalid argument";
+    case TMOE_ERR_UNSUPPORTED: return "unsupported shape or bit width";
+    case TMOE_ERR_SCRATCH: return "scratch arena too short or not 16-byte aligned";
+    case TMOE_ERR_CAPACITY: return "token count above the planned capacity";
+    case TMOE_ERR_ALIGNMENT: return "device pointer misaligned";
+    case TMOE_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+tmoe_status tmoe_debug_decode(tmoe_plan_t p, const tmoe_weights* wt, int32_t expert, int32_t matrix,
+                              int32_t as_e4m3, void* out, void* stream) {
+  if (!p || !wt || !wt->payload || !out) return TMOE_ERR_INVALID_ARG;
+  if (expert < 0 || expert >= p->E || (matrix != 0 && matrix != 1) || (as_e4m3 != 0 && as_e4m3 != 1))
+    return TMOE_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(wt->payload, 16)) return TMOE_ERR_ALIGNMENT;
+  const int bits = p->bits[expert];
+  const int K = matrix ? p->I : p->H;
+  const int N = matrix ? p->H : 2 * p->I;
+  const uint16_t* words = wt->payload + p->offsets[expert] + (matrix ? 2LL * p->H * p->I * bits / 16 : 0);
+  (void)hipGetLastError();
+  launch_debug_decode(words, bits, K, N, as_e4m3, out, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
+}
+
+tmoe_status tmoe_debug_mxfp8(const float* in, int64_t rows, int32_t cols, uint8_t* q, uint8_t* e8m0, void* stream) {
+  if (!in || !q || !e8m0 || rows < 0 || cols <= 0 || cols % 32) return TMOE_ERR_INVALID_ARG;
+  if (!aligned(in, 4)) return TMOE_ERR_ALIGNMENT;
+  if (rows == 0) return TMOE_OK;
+  (void)hipGetLastError();
+  launch_debug_mxfp8(in, rows, cols, q, e8m0, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
+}
+
+tmoe_status tmoe_debug_rotate(float* data, int64_t rows, int32_t n, void* stream) {
+  if (!data || rows < 0) return TMOE_ERR_INVALID_ARG;
+  if (!dim_ok(n)) return TMOE_ERR_UNSUPPORTED;
+  if (!aligned(data, 4)) return TMOE_ERR_ALIGNMENT;
+  if (rows == 0) return TMOE_OK;
+  (void)hipGetLastError();
+  launch_debug_rotate(data, rows, make_rot(n, 0), static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
+}
+
+tmoe_status tmoe_debug_get_views(tmoe_plan_t p, int32_t T, int32_t w4a8, void* scratch, size_t bytes,
+                                 tmoe_debug_views* out) {
+  if (!p || !out || T < 0 || (w4a8 != 0 && w4a8 != 1)) return TMOE_ERR_INVALID_ARG;
+  if (T > p->max_tokens) return TMOE_ERR_CAPACITY;
+  tmoe_status st = check_scratch(p, scratch, bytes);
+  if (st != TMOE_OK) return st;
+  const long long R = static_cast<long long>(T) * p->K;
+  out->a1 = at<void>(scratch, p->lay.a1);
+  out->a1_scale = at<uint8_t>(scratch, p->lay.a1) + static_cast<size_t>(R) * p->H;
+  out->z = at<float>(scratch, p->lay.z);
+  out->b = at<void>(scratch, p->lay.b);
+  out->b_scale = at<uint8_t>(scratch, p->lay.b) + static_cast<size_t>(R) * p->I;
+  out->v = at<float>(scratch, p->lay.v);
+  const int kdiv = w4a8 ? 128 : 32;
+  out->splits1 = choose_splits(R, p->H / kdiv);
+  out->splits2 = choose_splits(R, p->I / kdiv);
+  return TMOE_OK;
+}
+
+}  // extern "C"

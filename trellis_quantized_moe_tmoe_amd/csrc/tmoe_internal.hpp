@@ -1,0 +1,118 @@
+// tmoe_internal.hpp -- launch-argument structs and launchers shared by the host code and kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tmoe {
+
+struct ExpertInfo;
+
+struct RouteMapArgs {
+  const void* ids;
+  int ids64;
+  int routes;               // T * k
+  int num_experts;
+  int block_m;              // exported tile table
+  int gemm_rows;            // internal GEMM tile table
+  long long words_per_bit;  // 3*H*I/16: payload words of one expert per bit of width
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_routes;
+  int32_t* route_slot;
+  int32_t* tile_expert;
+  int32_t* tile_row0;
+  int32_t* tile_rows;
+  int32_t* num_tiles;
+  int32_t* status;
+  int4* gtiles;             // (expert, first slot, rows, 0)
+  int32_t* num_gtiles;
+  ExpertInfo* einfo;
+  uint32_t packed_bits[32]; // 2 bits per expert: bits - 2
+};
+
+// Rotation of a row of n values: one power-of-two block (pow2 = true, EPL = n / 64 values per
+// lane) or n / 128 blocks of 128 plus an optional 64-block.
+struct RowRot {
+  int n;
+  int pow2;
+  int nblk128;
+  int tail64;
+  int identity;
+};
+
+struct RotateArgs {          // a = R_H(su1_e * x_t) per slot, fp16 or MXFP8
+  const uint16_t* x;         // bf16 [T][H]
+  const void* ids;
+  int ids64;
+  int top_k;
+  const int32_t* sorted_routes;
+  const int32_t* offsets;    // offsets[E] = valid slots
+  int num_experts;
+  const uint16_t* su1;       // [E][H]
+  RowRot rot;
+  void* a1;                  // fp16 [R][H] or e4m3 [R][H]
+  uint8_t* a1_scale;         // [R][H/32]
+  int routes;
+};
+
+struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_I(z_u)))
+  const float* z;            // [splits][R][2I] unscaled partial sums
+  int splits;
+  const void* ids;
+  int ids64;
+  const int32_t* sorted_routes;
+  const int32_t* offsets;
+  int num_experts;
+  const uint16_t* scale1;    // [E][2I]
+  const uint16_t* sv1;       // [E][2I]
+  const uint16_t* su2;       // [E][I]
+  RowRot rot;                // n = I
+  void* b;                   // fp16 [R][I] or e4m3 [R][I]
+  uint8_t* b_scale;          // [R][I/32]
+  int routes;
+};
+
+struct CombineArgs {         // y_t = sum_j w[t,j] * sv2_e * R_H(scale2_e * v_slot)
+  const float* v;            // [splits][R][H]
+  int splits;
+  const void* ids;
+  int ids64;
+  const float* w;            // [T][k]
+  const int32_t* route_slot;
+  int top_k;
+  int tokens;
+  int routes;
+  const uint16_t* scale2;    // [E][H]
+  const uint16_t* sv2;       // [E][H]
+  RowRot rot;                // n = H
+  float* y;                  // [T][H]
+};
+
+struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slot][k] * C_e[k][n]
+  const uint16_t* payload;
+  const ExpertInfo* einfo;
+  long long fc2_words_per_bit;  // FC2 region starts after H*2I*bits/16 words: pass H*2I/16 or 0
+  const void* a;             // fp16 [R][K] or e4m3 [R][K]
+  const uint8_t* a_scale;    // [R][K/32] (fp8 only)
+  float* out;                // [splits][R][N]
+  const int4* gtiles;
+  const int32_t* num_gtiles;
+  int K, N;
+  int splits;
+  int routes;                // R: row stride between split planes
+};
+
+void launch_route_map(const RouteMapArgs& a, hipStream_t s);
+void launch_rotate(const RotateArgs& a, bool mx, hipStream_t s);
+void launch_act(const ActArgs& a, bool mx, hipStream_t s);
+void launch_combine(const CombineArgs& a, hipStream_t s);
+// mg: 16-row groups per GEMM tile (1, 2 or 4); waves: persistent wave count
+void launch_gemm_f16(const GemmArgs& a, int mg, int waves, hipStream_t s);
+void launch_gemm_f8(const GemmArgs& a, int mg, int waves, hipStream_t s);
+
+void launch_debug_decode(const uint16_t* matrix_words, int bits, int K, int N, int as_e4m3, void* out,
+                         hipStream_t s);
+void launch_debug_mxfp8(const float* in, long long rows, int cols, uint8_t* q, uint8_t* e8m0, hipStream_t s);
+void launch_debug_rotate(float* data, long long rows, const RowRot& rot, hipStream_t s);
+
+}  // namespace tmoe

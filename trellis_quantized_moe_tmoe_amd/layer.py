@@ -1,0 +1,166 @@
+"""Thin torch-facing wrapper over the C ABI: torch provides device memory and the stream only.
+
+Every step of the layer runs in the HIP kernels of libtmoe.so; this module only passes tensor
+pointers, sizes and the current stream."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import native
+from .native import check, lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class DeviceWeights:
+    """Device copies of one weight set: trellis payload words, fp16 scales and sign vectors."""
+
+    FIELDS = ("payload", "scale1", "scale2", "su1", "sv1", "su2", "sv2")
+
+    def __init__(self, payload: torch.Tensor, scale1, scale2, su1, sv1, su2, sv2):
+        self.payload, self.scale1, self.scale2 = payload, scale1, scale2
+        self.su1, self.sv1, self.su2, self.sv2 = su1, sv1, su2, sv2
+        self._c = native.Weights(*[t.data_ptr() for t in (payload, scale1, scale2, su1, sv1, su2, sv2)])
+
+    @classmethod
+    def from_inputs(cls, inp, device="cuda") -> "DeviceWeights":
+        def up(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+        return cls(up(inp.payload, np.int16), *[up(getattr(inp, n), np.float16)
+                                                 for n in ("scale1", "scale2", "su1", "sv1", "su2", "sv2")])
+
+    def clone(self) -> "DeviceWeights":
+        return DeviceWeights(*[getattr(self, n).clone() for n in self.FIELDS])
+
+    @property
+    def c(self) -> native.Weights:
+        return self._c
+
+
+def device_activations(inp, device="cuda", ids_dtype=torch.int64):
+    """(x as bf16 bit patterns in an int16 tensor [T, H], ids [T, k], weights fp32 [T, k])."""
+    x = torch.from_numpy(np.ascontiguousarray(inp.x_bf16).view(np.int16)).to(device)
+    ids = torch.from_numpy(np.ascontiguousarray(inp.ids)).to(ids_dtype).to(device)
+    w = torch.from_numpy(np.ascontiguousarray(inp.weights, np.float32)).to(device)
+    return x, ids, w
+
+
+class Plan:
+    def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int, max_tokens: int,
+                 expert_bits, rotation: str = "hadamard", ids_dtype=torch.int64, block_m: int = 0):
+        bits = np.ascontiguousarray(np.asarray(expert_bits, dtype=np.uint8))
+        self._bits = bits
+        self.config = native.Config(hidden, inter, num_experts, top_k, max_tokens,
+                                    bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                    native.ROT_IDENTITY if rotation == "identity" else native.ROT_HADAMARD,
+                                    native.IDS_I64 if ids_dtype == torch.int64 else native.IDS_I32, block_m)
+        self.ids_dtype = ids_dtype
+        handle = ctypes.c_void_p()
+        sb, pw = ctypes.c_size_t(), ctypes.c_size_t()
+        check(lib.tmoe_plan(ctypes.byref(self.config), ctypes.byref(handle), ctypes.byref(sb), ctypes.byref(pw)),
+              "tmoe_plan")
+        self.handle = handle
+        self.scratch_bytes = sb.value
+        self.payload_words = pw.value
+        self.hidden, self.inter, self.num_experts, self.top_k = hidden, inter, num_experts, top_k
+        self.max_tokens = max_tokens
+
+    @classmethod
+    def for_inputs(cls, inp, max_tokens: Optional[int] = None, **kw) -> "Plan":
+        return cls(inp.hidden, inp.inter, inp.experts, inp.top_k, max_tokens or inp.tokens, inp.bits, **kw)
+
+    def close(self):
+        if getattr(self, "handle", None) and self.handle.value:
+            lib.tmoe_plan_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def info(self) -> native.PlanInfo:
+        out = native.PlanInfo()
+        check(lib.tmoe_plan_get_info(self.handle, ctypes.byref(out)), "tmoe_plan_get_info")
+        return out
+
+    def expert_offset(self, e: int) -> int:
+        out = ctypes.c_size_t()
+        check(lib.tmoe_plan_expert_offset(self.handle, e, ctypes.byref(out)), "tmoe_plan_expert_offset")
+        return out.value
+
+    def alloc_scratch(self, device="cuda") -> torch.Tensor:
+        return torch.empty(self.scratch_bytes, dtype=torch.uint8, device=device)
+
+    def forward(self, x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor, weights: DeviceWeights,
+                scratch: torch.Tensor, y: Optional[torch.Tensor] = None, w4a8: bool = False) -> torch.Tensor:
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.hidden), dtype=torch.float32, device=x.device)
+        fn = lib.tmoe_forward_w4a8 if w4a8 else lib.tmoe_forward_w4a16
+        check(fn(self.handle, _ptr(x), _ptr(ids), _ptr(w), T, ctypes.byref(weights.c), _ptr(y), _ptr(scratch),
+                 scratch.numel(), _stream(x.device)), "tmoe_forward_w4a8" if w4a8 else "tmoe_forward_w4a16")
+        return y
+
+    def forward_status(self, x, ids, w, T, weights, y, scratch, scratch_bytes, w4a8=False, stream=None) -> int:
+        """Raw status of a forward call with explicit (possibly invalid) arguments; for tests."""
+        fn = lib.tmoe_forward_w4a8 if w4a8 else lib.tmoe_forward_w4a16
+        wc = ctypes.byref(weights.c) if isinstance(weights, DeviceWeights) else weights
+        return fn(self.handle, x, ids, w, T, wc, y, scratch, scratch_bytes, stream)
+
+    def route_map(self, ids: torch.Tensor, scratch: torch.Tensor) -> native.RouteMap:
+        T = ids.shape[0]
+        view = native.RouteMap()
+        check(lib.tmoe_build_route_map(self.handle, _ptr(ids), T, _ptr(scratch), scratch.numel(),
+                                       ctypes.byref(view), _stream(ids.device)), "tmoe_build_route_map")
+        return view
+
+    def debug_decode(self, weights: DeviceWeights, expert: int, matrix: int, as_e4m3: bool = False) -> torch.Tensor:
+        K, N = (self.hidden, 2 * self.inter) if matrix == 0 else (self.inter, self.hidden)
+        dev = weights.payload.device
+        out = torch.empty((K, N), dtype=torch.uint8 if as_e4m3 else torch.int16, device=dev)
+        check(lib.tmoe_debug_decode(self.handle, ctypes.byref(weights.c), expert, matrix, int(as_e4m3), _ptr(out),
+                                    _stream(dev)), "tmoe_debug_decode")
+        return out
+
+    def debug_views(self, T: int, w4a8: bool, scratch: torch.Tensor) -> native.DebugViews:
+        v = native.DebugViews()
+        check(lib.tmoe_debug_get_views(self.handle, T, int(w4a8), _ptr(scratch), scratch.numel(), ctypes.byref(v)),
+              "tmoe_debug_get_views")
+        return v
+
+
+def debug_mxfp8(x: torch.Tensor):
+    """MXFP8 quantization of an fp32 [rows, cols] device tensor with the forward's quantizer."""
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    e = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    check(lib.tmoe_debug_mxfp8(_ptr(x), rows, cols, _ptr(q), _ptr(e), _stream(x.device)), "tmoe_debug_mxfp8")
+    return q, e
+
+
+def debug_rotate(x: torch.Tensor) -> torch.Tensor:
+    """Rotation R_n of each row of an fp32 [rows, n] device tensor, in place, with the forward's kernels."""
+    rows, n = x.shape
+    check(lib.tmoe_debug_rotate(_ptr(x), rows, n, _stream(x.device)), "tmoe_debug_rotate")
+    return x
+
+
+def scratch_view(scratch: torch.Tensor, ptr: int, shape, dtype) -> torch.Tensor:
+    """View of `shape` elements of `dtype` at device address `ptr` inside the scratch tensor."""
+    off = int(ptr) - scratch.data_ptr()
+    n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+    if off < 0 or off + n > scratch.numel():
+        raise ValueError("pointer outside the scratch arena")
+    return scratch[off:off + n].view(dtype).view(shape)
