@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the trellis-quantized routed MoE layer on one MI355X.
+
+One step = one forward of the whole layer (route map, input rotation, FC1, activation, FC2,
+combine) over one batch of synthetic inputs resident in HBM. The headline workload is the decode
+geometry (T=16 tokens, H=1024, I=512, E=96, top-8, 4-bit trellis, W4A16). Weight sets are cycled
+over enough copies that their footprint exceeds 1 GB (four times the 256 MB Infinity Cache), so
+weight bytes come from HBM.
+
+Timing: the K steps are captured into one hipGraph and replayed between two events on the launch
+stream. Per-stage durations come from K more forwards issued stage by stage with events between
+the stages on the same stream, queued behind a bounded spin kernel so the GPU runs them back to
+back; the dominant kernel's average duration gives the roofline figure.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2516.6
+MFMA_F8_PEAK_TFLOPS = 5033.2
+STAGES = ["route_map", "rotate", "fc1", "act", "fc2", "combine"]
+COPY_FOOTPRINT = 1.0e9
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
+    ap.add_argument("--workload", default="decode:16")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 256 MiB device copy (reference for memory counters)")
+    return ap.parse_args()
+
+
+class Bench:
+    """One workload: inputs, weight copies, plan and scratch on the device."""
+
+    def __init__(self, name: str, T: int, w4a8: bool):
+        import torch
+        from trellis_quantized_moe_tmoe_amd import layer as L
+        from trellis_quantized_moe_tmoe_amd.workloads import make_inputs
+        self.torch, self.L = torch, L
+        self.name, self.T, self.w4a8 = name, T, w4a8
+        self.inp = make_inputs(name, tokens=T)
+        self.plan = L.Plan.for_inputs(self.inp)
+        base = L.DeviceWeights.from_inputs(self.inp)
+        per_copy = sum(getattr(base, f).numel() * getattr(base, f).element_size() for f in base.FIELDS)
+        self.n_copies = max(1, math.ceil(COPY_FOOTPRINT / per_copy))
+        self.copies = [base] + [base.clone() for _ in range(self.n_copies - 1)]
+        self.x, self.ids, self.w = L.device_activations(self.inp)
+        self.scratch = self.plan.alloc_scratch()
+        self.y = torch.empty((T, self.inp.hidden), dtype=torch.float32, device="cuda")
+        H, I = self.inp.hidden, self.inp.inter
+        touched = np.unique(self.inp.ids)
+        bits = self.inp.bits[touched].astype(np.int64)
+        self.touched = int(touched.size)
+        self.fc1_bytes = int(np.sum(H * 2 * I * bits // 8))
+        self.fc2_bytes = int(np.sum(I * H * bits // 8))
+        self.flops_fc1 = 2.0 * self.inp.routes * H * 2 * I
+        self.flops_fc2 = 2.0 * self.inp.routes * I * H
+
+    def forward(self, i: int):
+        self.plan.forward(self.x, self.ids, self.w, self.copies[i % self.n_copies], self.scratch, y=self.y,
+                          w4a8=self.w4a8)
+
+    def stages(self, i: int, first: int, last: int):
+        self.plan.forward_stages(first, last, self.x, self.ids, self.w, self.copies[i % self.n_copies],
+                                 self.scratch, self.y, w4a8=self.w4a8)
+
+    def _graph_time(self, fn, n: int, reps: int = 3) -> float:
+        """Capture n calls of fn(i) into one graph; return the best per-call ms over `reps` replays."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(min(n, 3)):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                fn(i)
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / n)
+        del g
+        return best
+
+    def _staged_ms(self, n: int) -> dict:
+        """Per-stage ms over n full forwards, each issued as its six stages with timing events between
+        them on the launch stream. A bounded spin kernel holds the stream while every launch is queued,
+        so the GPU then runs them back to back and the events see GPU time, not host launch gaps."""
+        torch = self.torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(n)]
+        torch.cuda.synchronize()
+        hold_s = 0.2
+        torch.cuda._sleep(int(hold_s * 2.4e9))
+        t0 = time.perf_counter()
+        for i in range(n):
+            ev[i][0].record()
+            for k in range(len(STAGES)):
+                self.stages(i, k, k)
+                ev[i][k + 1].record()
+        enqueue_s = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        out = {}
+        for k, nm in enumerate(STAGES):
+            out[nm] = float(np.mean([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(n)]))
+        out["step_sum"] = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(n)]))
+        out["enqueued_within_hold"] = bool(enqueue_s < 0.8 * hold_s)
+        return out
+
+    def run(self, steps: int, warmup: int) -> dict:
+        torch = self.torch
+        for i in range(warmup):
+            self.forward(i)
+        torch.cuda.synchronize()
+        # headline: K steps in one graph, timed with events on the launch stream
+        ms_step = self._graph_time(self.forward, steps, reps=1)
+        stage_ms = self._staged_ms(steps)
+        return dict(ms_step=ms_step, stage_ms=stage_ms)
+
+
+def cpu_baseline(inp, budget_s: float = 15.0):
+    """The float64 oracle on host cores, repeated on the same workload for a bounded time."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    import oracle_np
+    oracle.load()
+    cores = min(16, os.cpu_count() or 1)
+    runs, t0, y = 0, time.perf_counter(), None
+    while True:
+        y = oracle_np.forward(inp, mode="w4a8" if inp.name == "w4a8" else "w4a16", nthreads=cores)
+        runs += 1
+        if time.perf_counter() - t0 >= budget_s or runs >= 20:
+            break
+    el = time.perf_counter() - t0
+    return dict(value=inp.tokens * runs / el, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{runs} full forward(s) of the same workload ({inp.tokens} tokens each), "
+                       f"float64, {el:.1f} s"), y
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    name, T = args.workload.split(":")
+    T = int(T)
+    b = Bench(name, T, w4a8=(name == "w4a8"))
+    r = b.run(args.steps, args.warmup)
+    ms = r["ms_step"]
+    st = r["stage_ms"]
+    fc1_gbs = b.fc1_bytes / (st["fc1"] * 1e-3) / 1e9
+    fc2_gbs = b.fc2_bytes / (st["fc2"] * 1e-3) / 1e9
+    H, I = b.inp.hidden, b.inp.inter
+    out = {
+        "metric": "routed tokens/s per MoE layer; decode weight GB/s & prefill TFLOP/s vs peak",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if b.w4a8 else "fp16",
+        "data": "synthetic",
+        "config": {"workload": f"{name} T={T} H={H} I={I} E={b.inp.experts} top-{b.inp.top_k} "
+                               f"trellis bits {sorted(set(b.inp.bits.tolist()))} "
+                               f"{'W4A8' if b.w4a8 else 'W4A16'}",
+                   "routes": b.inp.routes, "touched_experts": b.touched, "weight_copies": b.n_copies},
+        "roofline": {"bound": "hbm", "kernel": "k_gemm_f16 (FC1)" if not b.w4a8 else "k_gemm_f8 (FC1)",
+                     "achieved": fc1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fc1_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": b.fc1_bytes, "avg_launch_ms": st["fc1"]},
+        "stage_ms": st,
+        "fc2_gbs": fc2_gbs,
+        "gemm_pair_gbs": (b.fc1_bytes + b.fc2_bytes) / ((st["fc1"] + st["fc2"]) * 1e-3) / 1e9,
+    }
+    y = b.y.cpu().numpy()
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = src.numel() * 4
+        del src, dst
+    del b
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        from trellis_quantized_moe_tmoe_amd.workloads import make_inputs
+        cb, yref = cpu_baseline(make_inputs(name, tokens=T))
+        out["cpu_baseline"] = cb
+        out["parity_rel_err"] = float(np.max(np.abs(y - yref)) / np.max(np.abs(yref)))
+    if not args.no_extra:
+        extra = {}
+        for nm, t, w8 in (("prefill", 2048, False), ("w4a8", 64, True), ("wide", 16, False), ("decode", 1, False)):
+            e = Bench(nm, t, w8)
+            rr = e.run(max(5, args.steps // 5), 3)
+            s2 = rr["stage_ms"]
+            gemm_s = (s2["fc1"] + s2["fc2"]) * 1e-3
+            peak = MFMA_F8_PEAK_TFLOPS if w8 else MFMA_F16_PEAK_TFLOPS
+            tf = (e.flops_fc1 + e.flops_fc2) / gemm_s / 1e12
+            gbs = (e.fc1_bytes + e.fc2_bytes) / gemm_s / 1e9
+            extra[f"{nm}:{t}"] = {"tokens_per_s": t / (rr["ms_step"] * 1e-3), "ms_per_step": rr["ms_step"],
+                                  "gemm_tflops": tf, "gemm_tflops_frac": tf / peak, "gemm_weight_gbs": gbs,
+                                  "gemm_weight_gbs_frac": gbs / HBM_PEAK_GBS, "stage_ms": s2,
+                                  "touched_experts": e.touched, "weight_copies": e.n_copies}
+            del e
+            torch.cuda.empty_cache()
+        out["extra"] = extra
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -140,6 +140,16 @@ tmoe_status tmoe_forward_w4a8(tmoe_plan_t plan, const void *x_bf16, const void *
                               const float *topk_w, int32_t T, const tmoe_weights *weights,
                               float *y, void *scratch, size_t scratch_bytes, void *stream);
 
+/* Run only stages first..last (0 route map, 1 input rotation + quantize, 2 FC1, 3 activation,
+ * 4 FC2, 5 output rotation + combine) of tmoe_forward_w4a16 (w4a8 = 0) or tmoe_forward_w4a8
+ * (w4a8 = 1), with that call's arguments and checks. A stage reads what the earlier stages of a
+ * call with the same T, ids and precision left in scratch, so stages 0..5 issued in order, in one
+ * call or several, equal one forward call. Lets a caller put timing events between the launches. */
+tmoe_status tmoe_forward_stages(tmoe_plan_t plan, int32_t w4a8, int32_t first, int32_t last,
+                                const void *x_bf16, const void *topk_ids, const float *topk_w,
+                                int32_t T, const tmoe_weights *weights, float *y, void *scratch,
+                                size_t scratch_bytes, void *stream);
+
 const char *tmoe_status_str(tmoe_status s);
 
 /* ---- test hooks: expose single steps so their bit-exactness can be graded ---- */
@@ -161,15 +171,17 @@ tmoe_status tmoe_debug_rotate(float *rows_data, int64_t rows, int32_t n, void *s
 typedef struct {                 /* where a forward call leaves its intermediates, for tests */
   void *a1;                      /* [T*k][H] fp16 (W4A16) or E4M3 bytes (W4A8), slot order      */
   uint8_t *a1_scale;             /* [T*k][H/32] E8M0 (W4A8)                                      */
-  float *z;                      /* [splits1][T*k][2I] fp32 FC1 partial sums, unscaled, slot order */
+  float *z;                      /* [splits[0]][T*k][2I] fp32 FC1 partial sums, unscaled, slot order */
   void *b;                       /* [T*k][I] fp16 or E4M3, slot order                             */
   uint8_t *b_scale;              /* [T*k][I/32] E8M0 (W4A8)                                      */
-  float *v;                      /* [splits2][T*k][H] fp32 FC2 partial sums, unscaled, slot order */
-  int32_t splits1, splits2;
+  float *v;                      /* [splits[1]][T*k][H] fp32 FC2 partial sums, unscaled, slot order;
+                                    the combine stage overwrites plane 0 with w * sv2 * R_H(scale2 * v) */
+  int32_t *splits;               /* device [2]: K splits of FC1 and FC2, chosen by the route-map
+                                    kernel from the tile count (readable after the stream completes) */
 } tmoe_debug_views;
 
-/* Views of the intermediates a forward call with T tokens leaves in scratch; w4a8 selects the
- * precision (0 = tmoe_forward_w4a16, 1 = tmoe_forward_w4a8), which sets the split counts. */
+/* Views of the intermediates a forward call with T tokens leaves in scratch; w4a8 names the
+ * precision of that call (0 = tmoe_forward_w4a16, 1 = tmoe_forward_w4a8). */
 tmoe_status tmoe_debug_get_views(tmoe_plan_t plan, int32_t T, int32_t w4a8, void *scratch,
                                  size_t scratch_bytes, tmoe_debug_views *out);
 

@@ -205,7 +205,8 @@ def test_sampled_intermediates_prefill():
     torch.cuda.synchronize()
     route_slot = scratch_view(c.scratch, slots.route_slot, (R,), torch.int32).cpu().numpy()
     a1 = scratch_view(c.scratch, view.a1, (R, H), torch.float16)
-    z = scratch_view(c.scratch, view.z, (view.splits1, R, 2 * I), torch.float32)
+    splits1 = int(scratch_view(c.scratch, view.splits, (2,), torch.int32)[0].item())
+    z = scratch_view(c.scratch, view.z, (splits1, R, 2 * I), torch.float32)
     rng = np.random.default_rng(0)
     for r in rng.choice(R, size=12, replace=False):
         t, j = divmod(int(r), c.inp.top_k)

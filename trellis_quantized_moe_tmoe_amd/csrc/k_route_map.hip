@@ -133,10 +133,10 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
     }
     for (int t = 0; t < gtiles_e; ++t) {
       int4 g;
-      g.x = tid;
+      g.x = tid | (bits_e << 24);
       g.y = off_e + t * a.gemm_rows;
       g.z = min(a.gemm_rows, total_e - t * a.gemm_rows);
-      g.w = 0;
+      g.w = static_cast<int>(info.word_offset >> 8);   // expert regions start on 256-word multiples
       a.gtiles[goff_e + t] = g;
     }
   }
@@ -144,6 +144,8 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
     a.offsets[E] = n_valid;
     *a.num_tiles = n_tiles;
     *a.num_gtiles = n_gtiles;
+    for (int f = 0; f < 2; ++f)
+      a.splits[f] = gemm_splits(n_gtiles, a.split_cfg[f][0], a.split_cfg[f][1], a.split_cfg[f][2], a.split_cfg[f][3]);
     int bad = 0;
     for (int ww = 0; ww < kWaves; ++ww) bad += bad_w[ww];
     *a.status = bad;

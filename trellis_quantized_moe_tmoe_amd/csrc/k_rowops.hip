@@ -6,9 +6,10 @@
 //  k_act    : the activation epilogue between FC1 and FC2 in the pages' order
 //             R_I -> svh -> silu(gate) * up -> suh_down -> R_I ("integrate EXL3 Trellis into the
 //             fused W4A16 API", review of kernel.py), with the FC1 channel scales applied first.
-//  k_combine: y_t = sum over j ascending of w[t,j] * sv2_e * R_H(scale2_e * v): the output rotation
-//             and the exact top-k weighting, one token per wavefront, no atomics, so the summation
-//             order is fixed and repeated calls are bitwise identical.
+//  k_out_rotate + k_topk_sum: y_t = sum over j ascending of w[t,j] * sv2_e * R_H(scale2_e * v), the
+//             output rotation with exact top-k weighting. The rotation runs per route (one wavefront
+//             each), the sum per token and column in a fixed j order with no atomics, so repeated
+//             calls are bitwise identical.
 #include "tmoe_device.hpp"
 #include "tmoe_internal.hpp"
 
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void k_rotate(RotateArgs a) {
 template <bool MX>
 struct ActBody {
   const ActArgs& a;
-  int lane, p, e, I;
+  int lane, p, e, I, splits;
   template <int S>
   __device__ __forceinline__ void run(int off) {
     float zg[S], zu[S];
@@ -92,7 +93,7 @@ struct ActBody {
 #pragma unroll
     for (int i = 0; i < S; ++i) {
       float sg = 0.0f, su = 0.0f;
-      for (int s = 0; s < a.splits; ++s) {
+      for (int s = 0; s < splits; ++s) {
         sg += zr[s * plane + 64 * i];
         su += zr[s * plane + I + 64 * i];
       }
@@ -134,52 +135,65 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
   if (p >= a.routes || p >= a.offsets[a.num_experts]) return;
   const int r = a.sorted_routes[p];
   const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
-  ActBody<MX> body{a, lane, p, e, a.rot.n};
+  ActBody<MX> body{a, lane, p, e, a.rot.n, *a.splits};
   for_segments<EPL>(a.rot, body);
 }
 
-struct CombineBody {
+// Per route slot: o = w[r] * sv2_e * R_H(scale2_e * sum_s v_s), written over split plane 0 of the
+// same slot (each slot is read completely before it is written, by the same wavefront).
+struct OutRotBody {
   const CombineArgs& a;
-  int lane, t, H;
+  int lane, p, e, H, splits;
+  float wt;
   template <int S>
   __device__ __forceinline__ void run(int off) {
-    float acc[S];
-#pragma unroll
-    for (int i = 0; i < S; ++i) acc[i] = 0.0f;
     const size_t plane = static_cast<size_t>(a.routes) * H;
-    for (int j = 0; j < a.top_k; ++j) {
-      const int r = t * a.top_k + j;
-      const int p = a.route_slot[r];
-      if (p < 0) continue;                    // dropped route: contributes zero
-      const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
-      const float wt = a.w[r];
-      const float* vr = a.v + static_cast<size_t>(p) * H + off + lane;
-      const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + off + lane;
-      float vv[S];
+    float* vr = a.v + static_cast<size_t>(p) * H + off + lane;
+    const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + off + lane;
+    float vv[S];
 #pragma unroll
-      for (int i = 0; i < S; ++i) {
-        float s = 0.0f;
-        for (int sp = 0; sp < a.splits; ++sp) s += vr[sp * plane + 64 * i];
-        vv[i] = s * h2f(c2[64 * i]);
-      }
-      if (!a.rot.identity) fwht_segment<S>(vv, lane);
-      const uint16_t* sg = a.sv2 + static_cast<size_t>(e) * H + off + lane;
-#pragma unroll
-      for (int i = 0; i < S; ++i) acc[i] += wt * (vv[i] * h2f(sg[64 * i]));
+    for (int i = 0; i < S; ++i) {
+      float acc = 0.0f;
+      for (int sp = 0; sp < splits; ++sp) acc += vr[sp * plane + 64 * i];
+      vv[i] = acc * h2f(c2[64 * i]);
     }
-    float* yr = a.y + static_cast<size_t>(t) * H + off + lane;
+    if (!a.rot.identity) fwht_segment<S>(vv, lane);
+    const uint16_t* sg = a.sv2 + static_cast<size_t>(e) * H + off + lane;
 #pragma unroll
-    for (int i = 0; i < S; ++i) yr[64 * i] = acc[i];
+    for (int i = 0; i < S; ++i) vr[64 * i] = wt * (vv[i] * h2f(sg[64 * i]));
   }
 };
 
 template <int EPL>
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+__global__ __launch_bounds__(256) void k_out_rotate(CombineArgs a) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.tokens) return;
-  CombineBody body{a, lane, t, a.rot.n};
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= a.routes || p >= a.offsets[a.num_experts]) return;
+  const int r = a.sorted_routes[p];
+  const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
+  OutRotBody body{a, lane, p, e, a.rot.n, *a.splits, a.w[r]};
   for_segments<EPL>(a.rot, body);
+}
+
+// y_t = sum over j ascending of o[slot(t, j)]; dropped routes add nothing. Four columns per thread.
+__global__ __launch_bounds__(256) void k_topk_sum(CombineArgs a) {
+  const int H4 = a.rot.n >> 2;
+  const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<long long>(a.tokens) * H4) return;
+  const int t = static_cast<int>(idx / H4), c = static_cast<int>(idx % H4);
+  const float4* o = reinterpret_cast<const float4*>(a.v);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < a.top_k; ++j) {
+    const int p = a.route_slot[t * a.top_k + j];
+    if (p >= 0) {
+      const float4 x = o[static_cast<size_t>(p) * H4 + c];
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+  }
+  reinterpret_cast<float4*>(a.y)[static_cast<size_t>(t) * H4 + c] = acc;
 }
 
 struct DebugRotateBody {
@@ -266,8 +280,10 @@ void launch_act(const ActArgs& a, bool mx, hipStream_t s) {
 void launch_combine(const CombineArgs& a, hipStream_t s) {
   dispatch_epl(a.rot, [&](auto epl) {
     constexpr int E = decltype(epl)::value;
-    hipLaunchKernelGGL((k_combine<E>), dim3(blocks_for(a.tokens)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_out_rotate<E>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
   });
+  const long long n = static_cast<long long>(a.tokens) * (a.rot.n / 4);
+  hipLaunchKernelGGL(k_topk_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a);
 }
 
 void launch_debug_rotate(float* data, long long rows, const RowRot& rot, hipStream_t s) {

@@ -8,7 +8,9 @@
 //
 // Work unit of one wavefront: (GEMM tile = expert + up to 16*MG slots, 64 output columns, one K
 // split). Units are dealt round-robin to a persistent grid whose size is fixed on the host, so the
-// launch is graph-capturable although the tile count is only known on the device.
+// launch is graph-capturable although the tile count is only known on the device. Within a unit
+// the payload words and activation fragments of the next D steps are kept in flight in a register
+// ring, so decode of step k overlaps the memory latency of steps k+1 .. k+D.
 //
 // Operand layouts (gfx950, checked on hardware):
 //  * v_mfma_f32_16x16x32_f16: A lane l = row l%16, k = 8*(l/16)+[0,8); B lane l = column l%16,
@@ -25,64 +27,118 @@ namespace tmoe {
 namespace {
 
 constexpr int NS = 4;   // 16-column strips per wavefront unit (64 columns)
+constexpr int DF = 4;   // fp16 path: K steps in flight
+constexpr int D8 = 2;   // fp8 path: K steps in flight (each step is 4x deeper)
+
+// A wave-uniform global pointer held in scalar registers (loads through it use the global path with
+// a scalar base and a per-lane 32-bit offset).
+template <class T>
+using gptr = const T __attribute__((address_space(1)))*;
+
+template <class T>
+__device__ __forceinline__ gptr<T> uniform_ptr(const T* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v >> 32));
+  return reinterpret_cast<gptr<T>>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+// One wavefront unit of the fp16 GEMM. Every K step's operands arrive with direct global->LDS
+// loads (16 bytes per lane) into the wavefront's own slot of an LDS ring DF steps deep: the step's
+// trellis words (two 16-deep tile rows x NS strips = 2*NS*TW 32-bit words, 1 KB at 4 bits; lane L
+// copies chunk L) and its A fragments (MG x 1 KB; each lane copies exactly the 16 bytes it later
+// feeds to the MFMA). The memory pipeline thus holds DF steps per wavefront without registers, and
+// the only waits are on the ring. Rows of the A fragment beyond the tile are loaded from the tile's
+// last row and their output rows are never stored (an MFMA output row depends on its own A row
+// only), so no masking sits in the K loop.
+template <int MG>
+constexpr int ring_words() { return DF * (2 * NS * 32 + MG * 256); }
 
 template <int BITS, int MG>
-__device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng, int s, int lane) {
+__device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng, int s, int splits, int lane,
+                                         uint32_t* ring, uint32_t mask, uint32_t orv) {
   constexpr int TW = 8 * BITS;                         // 32-bit words per 16x16 tile
-  const ExpertInfo info = a.einfo[t.x];
-  const uint32_t* mat = reinterpret_cast<const uint32_t*>(a.payload + info.word_offset +
-                                                          a.fc2_words_per_bit * BITS);
+  constexpr int BW = 2 * NS * TW;                      // trellis words per K step
+  constexpr int STAGE = 2 * NS * 32 + MG * 256;        // words per ring slot (sized for 4 bits)
+  constexpr int CPT = TW / 4;                          // 16-byte chunks per tile
+  const long long woff = (static_cast<long long>(static_cast<unsigned>(t.w)) << 8);
   const int row0 = t.y, rows = t.z;
   const int NT = a.N >> 4;
   const int col = lane & 15, grp = lane >> 4;
   const int q = 2 * col + (grp & 1);                   // 8-element group inside the tile
-  const int kt_off = grp >> 1;
-  const int ksteps = (a.K >> 5) / a.splits;
+  const int ksteps = (a.K >> 5) / splits;
   const int ks0 = s * ksteps, ks1 = ks0 + ksteps;
   const int nt0 = ng * NS;
-  const _Float16* A = static_cast<const _Float16*>(a.a);
-
-  const _Float16* arow[MG];
-  bool aok[MG];
+  const gptr<uint32_t> mat = uniform_ptr(reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS) +
+                                         static_cast<size_t>(nt0) * TW);
+  const gptr<_Float16> A = uniform_ptr(static_cast<const _Float16*>(a.a) + static_cast<size_t>(row0) * a.K);
+  // staging of trellis words: lane L < BW/4 copies 16-byte chunk L, [tile row][strip][chunk] order
+  const bool stager = lane < BW / 4;
+  const int st_tile = lane / (NS * CPT), st_strip = (lane / CPT) % NS, st_chunk = lane % CPT;
+  const int st_off = (st_tile * NT + st_strip) * TW + 4 * st_chunk;          // words, relative to the step
+  const int kstride = 2 * NT * TW;                                            // words between K steps
+  // reading: window words of group q in tile row (grp>>1) of strip ns
+  const int j0 = window_word<BITS>(q);
+  const int rd_a = (grp >> 1) * NS * TW + (j0 < 0 ? j0 + TW : j0);
+  const int rd_b = (grp >> 1) * NS * TW + ((j0 + 1 == TW) ? 0 : j0 + 1);
+  int aoff[MG];
 #pragma unroll
-  for (int mg = 0; mg < MG; ++mg) {
-    const int r = 16 * mg + col;
-    aok[mg] = r < rows;
-    arow[mg] = A + static_cast<size_t>(row0 + (aok[mg] ? r : 0)) * a.K + 8 * grp;
-  }
+  for (int mg = 0; mg < MG; ++mg) aoff[mg] = min(16 * mg + col, rows - 1) * a.K + 8 * grp;
+
   f4 acc[MG][NS];
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) acc[mg][ns] = f4{0.f, 0.f, 0.f, 0.f};
 
-  uint32_t hi[NS], lo[NS];
-  auto load = [&](int ks, uint32_t(&h)[NS], uint32_t(&l)[NS]) {
-    const uint32_t* trow = mat + static_cast<size_t>((2 * ks + kt_off) * NT + nt0) * TW;
+  auto issue = [&](int ks, int d) {
+    uint32_t* slot = ring + d * STAGE;
+    if (stager)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(mat + static_cast<size_t>(ks) * kstride + st_off),
+                                       (void __attribute__((address_space(3)))*)(slot), 16, 0, 0);
+    const gptr<_Float16> ab = A + 32 * ks;
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) load_window<BITS>(trow + ns * TW, q, h[ns], l[ns]);
+    for (int mg = 0; mg < MG; ++mg)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(ab + aoff[mg]),
+                                       (void __attribute__((address_space(3)))*)(slot + 2 * NS * 32 + mg * 256), 16, 0, 0);
   };
-  load(ks0, hi, lo);
-  for (int ks = ks0; ks < ks1; ++ks) {
-    uint32_t nhi[NS], nlo[NS];
-    load(ks + 1 < ks1 ? ks + 1 : ks, nhi, nlo);       // prefetch the next step (in bounds)
-    half8 b[NS];
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) b[ns] = decode8<BITS>(hi[ns], lo[ns], q);
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg) {
-      half8 av = *reinterpret_cast<const half8*>(arow[mg] + 32 * ks);
-      if (!aok[mg]) av = half8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-        acc[mg][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[ns], acc[mg][ns], 0, 0, 0);
-    }
+  auto step = [&](int d, int next) {
+    // the direct loads of the DF-1 younger steps may still be in flight
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DF - 1) * (1 + MG)) : "memory");
+    const uint32_t* slot = ring + d * STAGE;
+    uint32_t wh[NS], wl[NS];
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
-      hi[ns] = nhi[ns];
-      lo[ns] = nlo[ns];
+      wh[ns] = slot[rd_a + ns * TW];
+      wl[ns] = slot[rd_b + ns * TW];
     }
+    half8 aa[MG];
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) aa[mg] = *reinterpret_cast<const half8*>(slot + 2 * NS * 32 + mg * 256 + 4 * lane);
+    half8 b[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) b[ns] = decode8<BITS>(wh[ns], wl[ns], q, mask, orv);
+    // every LDS read of this slot has returned before the slot is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue(next, d);
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+        acc[mg][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aa[mg], b[ns], acc[mg][ns], 0, 0, 0);
+  };
+#pragma unroll
+  for (int d = 0; d < DF; ++d) issue(min(ks0 + d, ks1 - 1), d);
+  int base = ks0;
+  for (; base + DF <= ks1; base += DF) {
+#pragma unroll
+    for (int d = 0; d < DF; ++d) step(d, min(base + d + DF, ks1 - 1));
   }
+#pragma unroll
+  for (int d = 0; d < DF; ++d)
+    if (base + d < ks1) step(d, ks1 - 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // no load may still target the ring
+
   float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg)
@@ -96,57 +152,62 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
     }
 }
 
-template <int MG>
+// BITS = 0: experts of mixed widths, chosen per unit. FC (1 or 2) only names the instantiation,
+// so profiles tell the two GEMMs apart.
+template <int BITS, int MG, int FC>
 __global__ __launch_bounds__(256) void k_gemm_f16(GemmArgs a) {
+  __shared__ uint32_t ring_all[4 * ring_words<MG>()];  // one ring per wavefront
   const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wv);
   const int W = gridDim.x * 4;
   const int NG = a.N / (16 * NS);
-  const int units = *a.num_gtiles * NG * a.splits;
+  const int ntiles = *a.num_gtiles;
+  const int splits = *a.splits;
+  const int units = ntiles * NG * splits;
+  uint32_t* ring = ring_all + wv * ring_words<MG>();
+  const uint32_t mask = vreg_const(kMcgMask), orv = kMcgOr;
   for (int u = gw; u < units; u += W) {
-    const int s = u % a.splits;
-    const int rest = u / a.splits;
+    const int s = u % splits;
+    const int rest = u / splits;
     const int ng = rest % NG;
     const int4 t = a.gtiles[rest / NG];
-    const int bits = a.einfo[t.x].bits;
-    if (bits == 4) unit_f16<4, MG>(a, t, ng, s, lane);
-    else if (bits == 3) unit_f16<3, MG>(a, t, ng, s, lane);
-    else unit_f16<2, MG>(a, t, ng, s, lane);
+    if constexpr (BITS != 0) {
+      unit_f16<BITS, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
+    } else {
+      const int bits = (t.x >> 24) & 0xff;
+      if (bits == 4) unit_f16<4, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
+      else if (bits == 3) unit_f16<3, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
+      else unit_f16<2, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
+    }
   }
 }
 
 // 32 E4M3 weights of one lane for one 128-deep K step: tiles kt0 (bytes 0-15) and kt0+4
-// (bytes 16-31) of one column, 16 consecutive elements of each.
+// (bytes 16-31) of one column, 16 consecutive elements of each (groups 2*col and 2*col+1).
 template <int BITS>
-__device__ __forceinline__ i8v decode_b_f8(const uint32_t* tile0, const uint32_t* tile1, int col) {
-  uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-  load_window<BITS>(tile0, 2 * col, h0, l0);
-  load_window<BITS>(tile0, 2 * col + 1, h1, l1);
-  load_window<BITS>(tile1, 2 * col, h2, l2);
-  load_window<BITS>(tile1, 2 * col + 1, h3, l3);
+__device__ __forceinline__ i8v decode_b_f8(const uint32_t (&w)[8], int col, uint32_t mask, uint32_t orv) {
   i8v b;
-  uint32_t w0, w1;
-  fp8x8_from_half8(decode8<BITS>(h0, l0, 2 * col), w0, w1);
-  b[0] = static_cast<int>(w0); b[1] = static_cast<int>(w1);
-  fp8x8_from_half8(decode8<BITS>(h1, l1, 2 * col + 1), w0, w1);
-  b[2] = static_cast<int>(w0); b[3] = static_cast<int>(w1);
-  fp8x8_from_half8(decode8<BITS>(h2, l2, 2 * col), w0, w1);
-  b[4] = static_cast<int>(w0); b[5] = static_cast<int>(w1);
-  fp8x8_from_half8(decode8<BITS>(h3, l3, 2 * col + 1), w0, w1);
-  b[6] = static_cast<int>(w0); b[7] = static_cast<int>(w1);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint32_t p[4];
+    decode8_pairs<BITS>(w[2 * g], w[2 * g + 1], 2 * col + (g & 1), mask, orv, p);
+    b[2 * g] = static_cast<int>(fp8x4_from_pairs(p[0], p[1]));
+    b[2 * g + 1] = static_cast<int>(fp8x4_from_pairs(p[2], p[3]));
+  }
   return b;
 }
 
 template <int BITS, int MG>
-__device__ __forceinline__ void unit_f8(const GemmArgs& a, const int4 t, int ng, int s, int lane) {
+__device__ __forceinline__ void unit_f8(const GemmArgs& a, const int4 t, int ng, int s, int splits, int lane,
+                                        uint32_t mask, uint32_t orv) {
   constexpr int TW = 8 * BITS;
-  const ExpertInfo info = a.einfo[t.x];
-  const uint32_t* mat = reinterpret_cast<const uint32_t*>(a.payload + info.word_offset +
-                                                          a.fc2_words_per_bit * BITS);
+  const long long woff = (static_cast<long long>(static_cast<unsigned>(t.w)) << 8);
+  const uint32_t* mat = reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS);
   const int row0 = t.y, rows = t.z;
   const int NT = a.N >> 4;
   const int col = lane & 15, grp = lane >> 4;
-  const int ksteps = (a.K >> 7) / a.splits;
+  const int ksteps = (a.K >> 7) / splits;
   const int ks0 = s * ksteps, ks1 = ks0 + ksteps;
   const int nt0 = ng * NS;
   const uint8_t* A = static_cast<const uint8_t*>(a.a);
@@ -169,28 +230,57 @@ __device__ __forceinline__ void unit_f8(const GemmArgs& a, const int4 t, int ng,
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) acc[mg][ns] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = ks0; ks < ks1; ++ks) {
+  uint32_t w[D8][NS][8];
+  uint4 alo[D8][MG], ahi[D8][MG];
+  int asc[D8][MG];
+  auto load = [&](int ks, uint32_t(&ww)[NS][8], uint4(&lo)[MG], uint4(&hi)[MG], int(&sc)[MG]) {
     const int kt0 = 8 * ks + grp;
     const uint32_t* r0 = mat + static_cast<size_t>(kt0 * NT + nt0) * TW;
     const uint32_t* r1 = mat + static_cast<size_t>((kt0 + 4) * NT + nt0) * TW;
-    i8v b[NS];
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) b[ns] = decode_b_f8<BITS>(r0 + ns * TW, r1 + ns * TW, col);
+    for (int ns = 0; ns < NS; ++ns) {
+      load_window<BITS>(r0 + ns * TW, 2 * col, ww[ns][0], ww[ns][1]);
+      load_window<BITS>(r0 + ns * TW, 2 * col + 1, ww[ns][2], ww[ns][3]);
+      load_window<BITS>(r1 + ns * TW, 2 * col, ww[ns][4], ww[ns][5]);
+      load_window<BITS>(r1 + ns * TW, 2 * col + 1, ww[ns][6], ww[ns][7]);
+    }
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(arow[mg] + 128 * ks);
-      const uint4 hi = *reinterpret_cast<const uint4*>(arow[mg] + 128 * ks + 64);
-      i8v av = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
-      int sa = srow[mg][4 * ks];
-      if (!aok[mg]) {
-        av = i8v{0, 0, 0, 0, 0, 0, 0, 0};
-        sa = 127;
-      }
+      lo[mg] = *reinterpret_cast<const uint4*>(arow[mg] + 128 * ks);
+      hi[mg] = *reinterpret_cast<const uint4*>(arow[mg] + 128 * ks + 64);
+      sc[mg] = srow[mg][4 * ks];
+    }
+  };
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-        acc[mg][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b[ns], acc[mg][ns], 0, 0, 0, sa,
-                                                                      0, 127);
+  for (int d = 0; d < D8; ++d) load(min(ks0 + d, ks1 - 1), w[d], alo[d], ahi[d], asc[d]);
+  for (int base = ks0; base < ks1; base += D8) {
+#pragma unroll
+    for (int d = 0; d < D8; ++d) {
+      if (base + d < ks1) {
+        i8v b[NS];
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) b[ns] = decode_b_f8<BITS>(w[d][ns], col, mask, orv);
+        i8v av[MG];
+        int sa[MG];
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) {
+          const uint4 lo = alo[d][mg], hi = ahi[d][mg];
+          av[mg] = i8v{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                       static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+          sa[mg] = asc[d][mg];
+          if (!aok[mg]) {
+            av[mg] = i8v{0, 0, 0, 0, 0, 0, 0, 0};
+            sa[mg] = 127;
+          }
+        }
+        load(min(base + d + D8, ks1 - 1), w[d], alo[d], ahi[d], asc[d]);
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns)
+            acc[mg][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[mg], b[ns], acc[mg][ns], 0, 0, 0,
+                                                                          sa[mg], 0, 127);
+      }
     }
   }
   float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
@@ -206,26 +296,32 @@ __device__ __forceinline__ void unit_f8(const GemmArgs& a, const int4 t, int ng,
     }
 }
 
-template <int MG>
+template <int BITS, int MG, int FC>
 __global__ __launch_bounds__(256) void k_gemm_f8(GemmArgs a) {
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int W = gridDim.x * 4;
   const int NG = a.N / (16 * NS);
-  const int units = *a.num_gtiles * NG * a.splits;
+  const int splits = *a.splits;
+  const int units = *a.num_gtiles * NG * splits;
+  const uint32_t mask = vreg_const(kMcgMask), orv = kMcgOr;
   for (int u = gw; u < units; u += W) {
-    const int s = u % a.splits;
-    const int rest = u / a.splits;
+    const int s = u % splits;
+    const int rest = u / splits;
     const int ng = rest % NG;
     const int4 t = a.gtiles[rest / NG];
-    const int bits = a.einfo[t.x].bits;
-    if (bits == 4) unit_f8<4, MG>(a, t, ng, s, lane);
-    else if (bits == 3) unit_f8<3, MG>(a, t, ng, s, lane);
-    else unit_f8<2, MG>(a, t, ng, s, lane);
+    if constexpr (BITS != 0) {
+      unit_f8<BITS, MG>(a, t, ng, s, splits, lane, mask, orv);
+    } else {
+      const int bits = (t.x >> 24) & 0xff;
+      if (bits == 4) unit_f8<4, MG>(a, t, ng, s, splits, lane, mask, orv);
+      else if (bits == 3) unit_f8<3, MG>(a, t, ng, s, splits, lane, mask, orv);
+      else unit_f8<2, MG>(a, t, ng, s, splits, lane, mask, orv);
+    }
   }
 }
 
-// Dense decode of one K x N matrix with the GEMM's own lane mapping (test hook).
+// Dense decode of one K x N matrix with the GEMM's own lane mapping and decode (test hook).
 template <int BITS>
 __global__ __launch_bounds__(256) void k_debug_decode(const uint16_t* words, int K, int N, int as_e4m3,
                                                       void* out) {
@@ -239,18 +335,20 @@ __global__ __launch_bounds__(256) void k_debug_decode(const uint16_t* words, int
   const int q = 2 * col + (grp & 1);
   const int kt = 2 * kp + (grp >> 1);
   const uint32_t* tile = reinterpret_cast<const uint32_t*>(words) + static_cast<size_t>(kt * NT + nt) * TW;
+  const uint32_t mask = vreg_const(kMcgMask);
   uint32_t hi, lo;
   load_window<BITS>(tile, q, hi, lo);
-  const half8 h = decode8<BITS>(hi, lo, q);
+  uint32_t p[4];
+  decode8_pairs<BITS>(hi, lo, q, mask, kMcgOr, p);
   const int k0 = 16 * kt + 8 * (grp & 1);
   const int n = 16 * nt + col;
   if (!as_e4m3) {
-    _Float16* o = static_cast<_Float16*>(out);
+    uint16_t* o = static_cast<uint16_t*>(out);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) o[static_cast<size_t>(k0 + jj) * N + n] = h[jj];
+    for (int jj = 0; jj < 8; ++jj)
+      o[static_cast<size_t>(k0 + jj) * N + n] = static_cast<uint16_t>(p[jj >> 1] >> (16 * (jj & 1)));
   } else {
-    uint32_t w0, w1;
-    fp8x8_from_half8(h, w0, w1);
+    const uint32_t w0 = fp8x4_from_pairs(p[0], p[1]), w1 = fp8x4_from_pairs(p[2], p[3]);
     uint8_t* o = static_cast<uint8_t*>(out);
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
@@ -260,20 +358,52 @@ __global__ __launch_bounds__(256) void k_debug_decode(const uint16_t* words, int
   }
 }
 
-}  // namespace
-
-void launch_gemm_f16(const GemmArgs& a, int mg, int waves, hipStream_t s) {
-  const dim3 grid((waves + 3) / 4), block(256);
-  if (mg >= 4) hipLaunchKernelGGL(k_gemm_f16<4>, grid, block, 0, s, a);
-  else if (mg == 2) hipLaunchKernelGGL(k_gemm_f16<2>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_gemm_f16<1>, grid, block, 0, s, a);
+template <int BITS, int FC>
+void launch_f16(const GemmArgs& a, int mg, dim3 grid, hipStream_t s) {
+  if (mg >= 4) hipLaunchKernelGGL((k_gemm_f16<BITS, 4, FC>), grid, dim3(256), 0, s, a);
+  else if (mg == 2) hipLaunchKernelGGL((k_gemm_f16<BITS, 2, FC>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_gemm_f16<BITS, 1, FC>), grid, dim3(256), 0, s, a);
 }
 
-void launch_gemm_f8(const GemmArgs& a, int mg, int waves, hipStream_t s) {
-  const dim3 grid((waves + 3) / 4), block(256);
-  if (mg >= 4) hipLaunchKernelGGL(k_gemm_f8<4>, grid, block, 0, s, a);
-  else if (mg == 2) hipLaunchKernelGGL(k_gemm_f8<2>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_gemm_f8<1>, grid, block, 0, s, a);
+template <int BITS, int FC>
+void launch_f8(const GemmArgs& a, int mg, dim3 grid, hipStream_t s) {
+  if (mg >= 4) hipLaunchKernelGGL((k_gemm_f8<BITS, 4, FC>), grid, dim3(256), 0, s, a);
+  else if (mg == 2) hipLaunchKernelGGL((k_gemm_f8<BITS, 2, FC>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_gemm_f8<BITS, 1, FC>), grid, dim3(256), 0, s, a);
+}
+
+template <int FC>
+void launch_f16_bits(const GemmArgs& a, int bits, int mg, dim3 grid, hipStream_t s) {
+  switch (bits) {
+    case 4: launch_f16<4, FC>(a, mg, grid, s); break;
+    case 3: launch_f16<3, FC>(a, mg, grid, s); break;
+    case 2: launch_f16<2, FC>(a, mg, grid, s); break;
+    default: launch_f16<0, FC>(a, mg, grid, s); break;
+  }
+}
+
+template <int FC>
+void launch_f8_bits(const GemmArgs& a, int bits, int mg, dim3 grid, hipStream_t s) {
+  switch (bits) {
+    case 4: launch_f8<4, FC>(a, mg, grid, s); break;
+    case 3: launch_f8<3, FC>(a, mg, grid, s); break;
+    case 2: launch_f8<2, FC>(a, mg, grid, s); break;
+    default: launch_f8<0, FC>(a, mg, grid, s); break;
+  }
+}
+
+}  // namespace
+
+void launch_gemm_f16(const GemmArgs& a, int fc, int bits, int mg, int waves, hipStream_t s) {
+  const dim3 grid((waves + 3) / 4);
+  if (fc == 1) launch_f16_bits<1>(a, bits, mg, grid, s);
+  else launch_f16_bits<2>(a, bits, mg, grid, s);
+}
+
+void launch_gemm_f8(const GemmArgs& a, int fc, int bits, int mg, int waves, hipStream_t s) {
+  const dim3 grid((waves + 3) / 4);
+  if (fc == 1) launch_f8_bits<1>(a, bits, mg, grid, s);
+  else launch_f8_bits<2>(a, bits, mg, grid, s);
 }
 
 void launch_debug_decode(const uint16_t* matrix_words, int bits, int K, int N, int as_e4m3, void* out,

@@ -29,19 +29,40 @@ struct ExpertInfo {          // written into scratch by the route-map kernel
 
 // ------------------------------------------------------------------ trellis decode
 // Codebook value of a 16-bit state s: m = ((s * 0xCBAC1FED) mod 2^32 & 0x8fff8fff) | 0x3b603b60,
-// value = h(lo16(m)) + h(hi16(m)) rounded once to fp16. With s < 2^16 the 32-bit product splits
-// into two 16 x 16 products that each fit 32 bits (so they map to the full-rate u24 multiply):
-// s*0xCBAC1FED = s*0x1FED + ((s*0xCBAC) << 16) mod 2^32.
+// value = h(lo16(m)) + h(hi16(m)) rounded once to fp16 (round to nearest even). The multiply is a
+// full-rate v_mul_lo_u32 on gfx950; mask and OR are one v_and_or_b32; the half + half sum is one
+// SDWA add that reads both halves of m and writes straight into one half of a packed operand.
+constexpr uint32_t kMcgMul = 0xCBAC1FEDu;
+constexpr uint32_t kMcgMask = 0x8fff8fffu;
+constexpr uint32_t kMcgOr = 0x3b603b60u;
+
+__device__ __forceinline__ uint32_t mcg_bits(uint32_t s, uint32_t mask, uint32_t orv) {
+  const uint32_t x = s * kMcgMul;
+  uint32_t m;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(m) : "v"(x), "v"(mask), "s"(orv));
+  return m;
+}
+
+// Two codebook values from their m words, packed as (value of ma) | (value of mb) << 16.
+__device__ __forceinline__ uint32_t code_pair(uint32_t ma, uint32_t mb) {
+  uint32_t r;
+  asm("v_add_f16_sdwa %0, %1, %1 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_1\n\t"
+      "v_add_f16_sdwa %0, %2, %2 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0 src1_sel:WORD_1"
+      : "=&v"(r)
+      : "v"(ma), "v"(mb));
+  return r;
+}
+
+// Codebook value of one state (scalar path, used where a single value is needed).
 __device__ __forceinline__ _Float16 trellis_code(uint32_t s) {
-  const uint32_t x = s * 0x1FEDu + ((s * 0xCBACu) << 16);
-  const uint32_t m = (x & 0x8fff8fffu) | 0x3b603b60u;
+  const uint32_t m = ((s * kMcgMul) & kMcgMask) | kMcgOr;
   const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(m & 0xffffu));
   const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(m >> 16));
   return lo + hi;
 }
 
 // Two little-endian 16-bit words in one 32-bit load, as a big-endian (first word high) bit string.
-__device__ __forceinline__ uint32_t be32(uint32_t w) { return (w << 16) | (w >> 16); }
+__device__ __forceinline__ uint32_t be32(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 16); }
 
 // 32-bit word index j0 (floor((q*BITS - 2) / 4), may be -1) of the 64-bit window that covers the
 // states of elements 8q .. 8q+7 of a tile: their bits span [8q*BITS + BITS - 16, 8q*BITS + 8*BITS).
@@ -52,8 +73,8 @@ __device__ __forceinline__ int window_word(int q) {
   else return (q * BITS - 2) >> 2;
 }
 
-// Load the window of group q of the tile starting at `tile` (8*BITS 32-bit words): hi/lo are the
-// big-endian halves of the 64 stream bits [32*j0, 32*j0 + 64), taken modulo the tile length.
+// Load the window of group q of the tile starting at `tile` (8*BITS 32-bit words): the raw words
+// holding stream bits [32*j0, 32*j0 + 64), taken modulo the tile length.
 template <int BITS>
 __device__ __forceinline__ void load_window(const uint32_t* __restrict__ tile, int q, uint32_t& hi,
                                             uint32_t& lo) {
@@ -65,25 +86,64 @@ __device__ __forceinline__ void load_window(const uint32_t* __restrict__ tile, i
   lo = tile[b];
 }
 
-// Decode elements 8q .. 8q+7 from a loaded window into fp16 codebook values.
+// The 16-bit states of elements 8q .. 8q+7 from a loaded window (raw words).
 template <int BITS>
-__device__ __forceinline__ half8 decode8(uint32_t hi_raw, uint32_t lo_raw, int q) {
-  const uint32_t hi = be32(hi_raw), lo = be32(lo_raw);
-  const int j0 = window_word<BITS>(q);
-  half8 r;
+__device__ __forceinline__ void window_states(uint32_t hi_raw, uint32_t lo_raw, int q, uint32_t (&st)[8]) {
+  if constexpr (BITS == 4) {
+    // words: hi_raw = w[2q-2] | w[2q-1] << 16, lo_raw = w[2q] | w[2q+1] << 16 (little endian).
+    // The state of element 8q+j is the 16 stream bits ending at 4(8q+j+1): with the big-endian
+    // strings X = w[2q-1]:w[2q] and L = w[2q]:w[2q+1] it is X >> (12-4j) for j < 3 and
+    // L >> (28-4j) for j >= 3, each masked to 16 bits.
+    const uint32_t X = __builtin_amdgcn_perm(hi_raw, lo_raw, 0x07060100u);   // bytes: lo.0 lo.1 hi.2 hi.3
+    const uint32_t L = be32(lo_raw);
+    st[0] = __builtin_amdgcn_ubfe(X, 12, 16);
+    st[1] = __builtin_amdgcn_ubfe(X, 8, 16);
+    st[2] = __builtin_amdgcn_ubfe(X, 4, 16);
+    st[3] = lo_raw & 0xffffu;
+    st[4] = __builtin_amdgcn_ubfe(L, 12, 16);
+    st[5] = __builtin_amdgcn_ubfe(L, 8, 16);
+    st[6] = __builtin_amdgcn_ubfe(L, 4, 16);
+    st[7] = lo_raw >> 16;
+  } else {
+    const uint32_t hi = be32(hi_raw), lo = be32(lo_raw);
+    const int j0 = window_word<BITS>(q);
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    // the state of element 8q+jj ends at stream bit (8q+jj+1)*BITS; in the window that is
-    // bit position end_rel from the top, so the state is (window >> (64 - end_rel)) & 0xffff.
-    const int shift = 64 - ((8 * q + jj + 1) * BITS - 32 * j0);
-    uint32_t w;
-    if constexpr (BITS == 4) {
-      w = __builtin_amdgcn_alignbit(hi, lo, 28 - 4 * jj);   // shift = 28 - 4*jj for every q
-    } else {
-      w = shift >= 32 ? (hi >> (shift - 32)) : __builtin_amdgcn_alignbit(hi, lo, shift);
+    for (int jj = 0; jj < 8; ++jj) {
+      // element 8q+jj's state ends at stream bit (8q+jj+1)*BITS, i.e. end_rel bits into the window
+      const int shift = 64 - ((8 * q + jj + 1) * BITS - 32 * j0);
+      const uint32_t w = shift >= 32 ? (hi >> (shift - 32)) : __builtin_amdgcn_alignbit(hi, lo, shift);
+      st[jj] = w & 0xffffu;
     }
-    r[jj] = trellis_code(w & 0xffffu);
   }
+}
+
+// Decode elements 8q .. 8q+7 into four packed fp16 pairs (element 8q+2i in the low half of p[i]).
+template <int BITS>
+__device__ __forceinline__ void decode8_pairs(uint32_t hi_raw, uint32_t lo_raw, int q, uint32_t mask,
+                                              uint32_t orv, uint32_t (&p)[4]) {
+  uint32_t st[8];
+  window_states<BITS>(hi_raw, lo_raw, q, st);
+  uint32_t m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m[j] = mcg_bits(st[j], mask, orv);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = code_pair(m[2 * i], m[2 * i + 1]);
+}
+
+template <int BITS>
+__device__ __forceinline__ half8 decode8(uint32_t hi_raw, uint32_t lo_raw, int q, uint32_t mask, uint32_t orv) {
+  uint32_t p[4];
+  decode8_pairs<BITS>(hi_raw, lo_raw, q, mask, orv, p);
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  const u4v v = {p[0], p[1], p[2], p[3]};
+  return __builtin_bit_cast(half8, v);
+}
+
+// The mask and OR constants live in registers for v_and_or_b32 (no 32-bit literal in VOP3 here);
+// loading them through an opaque move keeps them from being folded back into two instructions.
+__device__ __forceinline__ uint32_t vreg_const(uint32_t c) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
   return r;
 }
 
@@ -101,11 +161,25 @@ __device__ __forceinline__ uint32_t fp8x2_from_f32(float a, float b) {
   return static_cast<uint32_t>(static_cast<uint16_t>(r[0]));
 }
 
-// Eight fp16 codes -> eight E4M3 bytes (two 32-bit words).
-__device__ __forceinline__ void fp8x8_from_half8(half8 h, uint32_t& w0, uint32_t& w1) {
-  half2v p0 = {h[0], h[1]}, p1 = {h[2], h[3]}, p2 = {h[4], h[5]}, p3 = {h[6], h[7]};
-  w0 = fp8x2_from_half2(p0) | (fp8x2_from_half2(p1) << 16);
-  w1 = fp8x2_from_half2(p2) | (fp8x2_from_half2(p3) << 16);
+// Two packed fp16 pairs -> four E4M3 bytes in one word (pa's values in bytes 0-1, pb's in 2-3);
+// the second conversion writes the high half and keeps the low one.
+__device__ __forceinline__ uint32_t fp8x4_from_pairs(uint32_t pa, uint32_t pb) {
+  s2v r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(half2v, pa), 1.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(half2v, pb), 1.0f, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ------------------------------------------------------------------ work split
+// K splits of a grouped GEMM with `ntiles` route tiles and `ng` column groups: as many as keep the
+// unit count within the launched wavefronts (one round of units, no second-round tail), at most
+// `most`, and dividing the K steps so every split has the same depth.
+__device__ __forceinline__ int gemm_splits(int ntiles, int ng, int ksteps, int most, int waves) {
+  int s = 1;
+  const long long per_split = static_cast<long long>(ntiles) * ng;
+  while (2 * s <= most && per_split * 2 * s <= waves) s *= 2;
+  while (s > 1 && ksteps % s) s >>= 1;
+  return s;
 }
 
 // ------------------------------------------------------------------ conversions
@@ -119,17 +193,40 @@ __device__ __forceinline__ float h2f(uint16_t h) {
 // ------------------------------------------------------------------ wavefront FWHT
 // A row segment of 64*EPL values lives in a wavefront with element e = i*64 + lane in v[i].
 // The butterflies of the Walsh-Hadamard transform in natural order commute, so the cross-lane
-// strides 1..32 and the in-register strides 64..32*EPL can run in any order.
+// strides 1..32 and the in-register strides 64..32*EPL can run in any order. Cross-lane partners
+// come from DPP (strides 1, 2, 8), ds_swizzle (4, 16) and one lane permute (32); the butterfly is
+// then new = partner + sign * own with sign = -1 on the lane holding the upper element.
+template <int S>
+__device__ __forceinline__ float lane_partner(float v) {
+  const int x = __float_as_int(v);
+  int r;
+  if constexpr (S == 1) r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true);        // quad_perm 1,0,3,2
+  else if constexpr (S == 2) r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true);   // quad_perm 2,3,0,1
+  else if constexpr (S == 4) r = __builtin_amdgcn_ds_swizzle(x, 0x1F | (4 << 10));          // lane ^ 4
+  else if constexpr (S == 8) r = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, true);  // row_ror 8
+  else if constexpr (S == 16) r = __builtin_amdgcn_ds_swizzle(x, 0x1F | (16 << 10));        // lane ^ 16
+  else r = __shfl_xor(x, 32, 64);
+  return __int_as_float(r);
+}
+
+template <int S, int EPL>
+__device__ __forceinline__ void fwht_lane_stage(float (&v)[EPL], int lane) {
+  const float sg = (lane & S) ? -1.0f : 1.0f;
+  float p[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) p[i] = lane_partner<S>(v[i]);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) v[i] = fmaf(sg, v[i], p[i]);
+}
+
 template <int EPL>
 __device__ __forceinline__ void fwht_segment(float (&v)[EPL], int lane) {
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const float p = __shfl_xor(v[i], s, 64);
-      v[i] = (lane & s) ? (p - v[i]) : (v[i] + p);
-    }
-  }
+  fwht_lane_stage<1>(v, lane);
+  fwht_lane_stage<2>(v, lane);
+  fwht_lane_stage<4>(v, lane);
+  fwht_lane_stage<8>(v, lane);
+  fwht_lane_stage<16>(v, lane);
+  fwht_lane_stage<32>(v, lane);
 #pragma unroll
   for (int t = 1; t < EPL; t <<= 1) {
 #pragma unroll

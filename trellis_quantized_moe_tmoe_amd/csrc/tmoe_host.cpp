@@ -13,7 +13,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/tmoe.h"
+#include "tmoe.h"
 #include "tmoe_device.hpp"
 #include "tmoe_internal.hpp"
 
@@ -71,6 +71,7 @@ struct tmoe_plan_s {
   long long routes_max;
   int max_tiles, max_gtiles;
   bool fp8_ok;
+  int uniform_bits;                 // the width shared by all experts, or 0 if they differ
   Layout lay;
 };
 
@@ -97,7 +98,7 @@ void build_layout(tmoe_plan_s* p) {
   L.tile_e = take(4ull * p->max_tiles);
   L.tile_r0 = take(4ull * p->max_tiles);
   L.tile_rows = take(4ull * p->max_tiles);
-  L.scalars = take(16);                               // num_tiles, status, num_gtiles
+  L.scalars = take(32);                               // num_tiles, status, num_gtiles, splits[2]
   L.gtiles = take(16ull * p->max_gtiles);
   L.a1 = take(2ull * R * p->H);                       // fp16, or E4M3 + E8M0 planes
   const long long zrows = max_split_rows(R, p->H / 32, p->H / 128 > 0 ? p->H / 128 : 1);
@@ -136,8 +137,25 @@ tmoe_route_map make_view(const tmoe_plan_s* p, void* scratch) {
   return v;
 }
 
-void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_rows, void* scratch,
-                       hipStream_t st) {
+struct GemmShape {          // launch shape of one grouped GEMM
+  int ng, ksteps, most, waves;
+};
+
+// Column groups, K steps, split bound and persistent wavefronts of FC1 (fc = 1) or FC2 (fc = 2).
+GemmShape gemm_shape(const tmoe_plan_s* p, long long R, int gemm_rows, bool fp8, int fc) {
+  GemmShape g;
+  const int K = fc == 1 ? p->H : p->I;
+  const int N = fc == 1 ? 2 * p->I : p->H;
+  g.ng = N / 64;
+  g.ksteps = K / (fp8 ? 128 : 32);
+  g.most = choose_splits(R, g.ksteps);
+  const long long gt_ub = std::min<long long>(R, p->E + R / gemm_rows + 1);
+  g.waves = static_cast<int>(std::min<long long>(kGemmWaveCap, gt_ub * g.ng * g.most));
+  return g;
+}
+
+void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_rows, const GemmShape (&sh)[2],
+                       void* scratch, hipStream_t st) {
   RouteMapArgs a;
   std::memset(&a, 0, sizeof(a));
   a.ids = ids;
@@ -157,6 +175,13 @@ void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_ro
   a.num_tiles = at<int32_t>(scratch, p->lay.scalars);
   a.status = at<int32_t>(scratch, p->lay.scalars) + 1;
   a.num_gtiles = at<int32_t>(scratch, p->lay.scalars) + 2;
+  a.splits = at<int32_t>(scratch, p->lay.scalars) + 3;
+  for (int f = 0; f < 2; ++f) {
+    a.split_cfg[f][0] = sh[f].ng;
+    a.split_cfg[f][1] = sh[f].ksteps;
+    a.split_cfg[f][2] = sh[f].most;
+    a.split_cfg[f][3] = sh[f].waves;
+  }
   a.gtiles = at<int4>(scratch, p->lay.gtiles);
   a.einfo = at<ExpertInfo>(scratch, p->lay.einfo);
   std::memcpy(a.packed_bits, p->packed_bits, sizeof(a.packed_bits));
@@ -173,8 +198,10 @@ tmoe_status check_common(const tmoe_plan_s* p, const void* ids, int T, void* scr
   return check_scratch(p, scratch, bytes);
 }
 
+// Stages: 0 route map, 1 input rotation, 2 FC1, 3 activation, 4 FC2, 5 combine.
 tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* w, int32_t T,
-                    const tmoe_weights* wt, float* y, void* scratch, size_t bytes, void* stream, bool fp8) {
+                    const tmoe_weights* wt, float* y, void* scratch, size_t bytes, void* stream, bool fp8,
+                    int first = 0, int last = 5) {
   tmoe_status st = check_common(p, ids, T, scratch, bytes);
   if (st != TMOE_OK) return st;
   if (fp8 && !p->fp8_ok) return TMOE_ERR_UNSUPPORTED;
@@ -191,13 +218,12 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   const long long R = static_cast<long long>(T) * p->K;
   const int mg = choose_mg(R, p->E);
   const int gemm_rows = 16 * mg;
-  const int kdiv = fp8 ? 128 : 32;
-  const int s1 = choose_splits(R, p->H / kdiv);
-  const int s2 = choose_splits(R, p->I / kdiv);
-  const long long gt_ub = std::min<long long>(R, p->E + R / gemm_rows + 1);
+  const GemmShape sh[2] = {gemm_shape(p, R, gemm_rows, fp8, 1), gemm_shape(p, R, gemm_rows, fp8, 2)};
+  int32_t* splits_dev = at<int32_t>(scratch, p->lay.scalars) + 3;
 
   (void)hipGetLastError();   // clear a stale error so the check below reports this call only
-  enqueue_route_map(p, ids, T, gemm_rows, scratch, s);
+  auto on = [&](int stage) { return first <= stage && stage <= last; };
+  if (on(0)) enqueue_route_map(p, ids, T, gemm_rows, sh, scratch, s);
 
   const int32_t* sorted = at<int32_t>(scratch, p->lay.sorted);
   const int32_t* offsets = at<int32_t>(scratch, p->lay.offsets);
@@ -221,7 +247,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   ra.a1 = a1;
   ra.a1_scale = a1s;
   ra.routes = static_cast<int>(R);
-  launch_rotate(ra, fp8, s);
+  if (on(1)) launch_rotate(ra, fp8, s);
 
   GemmArgs g1;
   g1.payload = wt->payload;
@@ -234,15 +260,17 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g1.num_gtiles = at<int32_t>(scratch, p->lay.scalars) + 2;
   g1.K = p->H;
   g1.N = 2 * p->I;
-  g1.splits = s1;
+  g1.splits = splits_dev;
   g1.routes = static_cast<int>(R);
-  const int waves1 = static_cast<int>(std::min<long long>(kGemmWaveCap, gt_ub * (g1.N / 64) * s1));
-  if (fp8) launch_gemm_f8(g1, mg, waves1, s);
-  else launch_gemm_f16(g1, mg, waves1, s);
+  const int waves1 = sh[0].waves;
+  if (on(2)) {
+    if (fp8) launch_gemm_f8(g1, 1, p->uniform_bits, mg, waves1, s);
+    else launch_gemm_f16(g1, 1, p->uniform_bits, mg, waves1, s);
+  }
 
   ActArgs aa;
   aa.z = z;
-  aa.splits = s1;
+  aa.splits = splits_dev;
   aa.ids = ids;
   aa.ids64 = p->ids64;
   aa.sorted_routes = sorted;
@@ -255,7 +283,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   aa.b = bq;
   aa.b_scale = bs;
   aa.routes = static_cast<int>(R);
-  launch_act(aa, fp8, s);
+  if (on(3)) launch_act(aa, fp8, s);
 
   GemmArgs g2 = g1;
   g2.fc2_words_per_bit = 2LL * p->H * p->I / 16;
@@ -264,18 +292,23 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g2.out = v;
   g2.K = p->I;
   g2.N = p->H;
-  g2.splits = s2;
-  const int waves2 = static_cast<int>(std::min<long long>(kGemmWaveCap, gt_ub * (g2.N / 64) * s2));
-  if (fp8) launch_gemm_f8(g2, mg, waves2, s);
-  else launch_gemm_f16(g2, mg, waves2, s);
+  g2.splits = splits_dev + 1;
+  const int waves2 = sh[1].waves;
+  if (on(4)) {
+    if (fp8) launch_gemm_f8(g2, 2, p->uniform_bits, mg, waves2, s);
+    else launch_gemm_f16(g2, 2, p->uniform_bits, mg, waves2, s);
+  }
 
   CombineArgs ca;
   ca.v = v;
-  ca.splits = s2;
+  ca.splits = splits_dev + 1;
   ca.ids = ids;
   ca.ids64 = p->ids64;
   ca.w = w;
   ca.route_slot = at<int32_t>(scratch, p->lay.slot);
+  ca.sorted_routes = sorted;
+  ca.offsets = offsets;
+  ca.num_experts = p->E;
   ca.top_k = p->K;
   ca.tokens = T;
   ca.routes = static_cast<int>(R);
@@ -283,7 +316,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   ca.sv2 = wt->sv2;
   ca.rot = make_rot(p->H, p->rotation == TMOE_ROT_IDENTITY);
   ca.y = y;
-  launch_combine(ca, s);
+  if (on(5)) launch_combine(ca, s);
 
   return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
 }
@@ -334,6 +367,9 @@ tmoe_status tmoe_plan(const tmoe_config* cfg, tmoe_plan_t* out, size_t* scratch_
   p->max_tiles = static_cast<int>(rmax / p->block_m + p->E + 1);
   p->max_gtiles = static_cast<int>(rmax / 16 + p->E + 1);
   p->fp8_ok = (p->H % 128 == 0) && (p->I % 128 == 0);
+  p->uniform_bits = p->bits[0];
+  for (int e = 1; e < p->E; ++e)
+    if (p->bits[e] != p->bits[0]) p->uniform_bits = 0;
   build_layout(p);
   *out = p;
   if (scratch_bytes) *scratch_bytes = p->lay.total;
@@ -369,8 +405,10 @@ tmoe_status tmoe_build_route_map(tmoe_plan_t p, const void* ids, int32_t T, void
   if (!view) return TMOE_ERR_INVALID_ARG;
   if (T == 0) return TMOE_OK;
   const long long R = static_cast<long long>(T) * p->K;
+  const int gemm_rows = 16 * choose_mg(R, p->E);
+  const GemmShape sh[2] = {gemm_shape(p, R, gemm_rows, false, 1), gemm_shape(p, R, gemm_rows, false, 2)};
   (void)hipGetLastError();
-  enqueue_route_map(p, ids, T, 16 * choose_mg(R, p->E), scratch, static_cast<hipStream_t>(stream));
+  enqueue_route_map(p, ids, T, gemm_rows, sh, scratch, static_cast<hipStream_t>(stream));
   *view = make_view(p, scratch);
   return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
 }
@@ -383,6 +421,13 @@ tmoe_status tmoe_forward_w4a16(tmoe_plan_t p, const void* x, const void* ids, co
 tmoe_status tmoe_forward_w4a8(tmoe_plan_t p, const void* x, const void* ids, const float* w, int32_t T,
                               const tmoe_weights* wt, float* y, void* scratch, size_t bytes, void* stream) {
   return forward(p, x, ids, w, T, wt, y, scratch, bytes, stream, true);
+}
+
+tmoe_status tmoe_forward_stages(tmoe_plan_t p, int32_t w4a8, int32_t first, int32_t last, const void* x,
+                                const void* ids, const float* w, int32_t T, const tmoe_weights* wt, float* y,
+                                void* scratch, size_t bytes, void* stream) {
+  if ((w4a8 != 0 && w4a8 != 1) || first < 0 || last > 5 || first > last) return TMOE_ERR_INVALID_ARG;
+  return forward(p, x, ids, w, T, wt, y, scratch, bytes, stream, w4a8 != 0, first, last);
 }
 
 const char* tmoe_status_str(tmoe_status s) {
@@ -445,9 +490,7 @@ tmoe_status tmoe_debug_get_views(tmoe_plan_t p, int32_t T, int32_t w4a8, void* s
   out->b = at<void>(scratch, p->lay.b);
   out->b_scale = at<uint8_t>(scratch, p->lay.b) + static_cast<size_t>(R) * p->I;
   out->v = at<float>(scratch, p->lay.v);
-  const int kdiv = w4a8 ? 128 : 32;
-  out->splits1 = choose_splits(R, p->H / kdiv);
-  out->splits2 = choose_splits(R, p->I / kdiv);
+  out->splits = at<int32_t>(scratch, p->lay.scalars) + 3;
   return TMOE_OK;
 }
 

@@ -24,8 +24,10 @@ struct RouteMapArgs {
   int32_t* tile_rows;
   int32_t* num_tiles;
   int32_t* status;
-  int4* gtiles;             // (expert, first slot, rows, 0)
+  int4* gtiles;             // (expert | bits << 24, first slot, rows, payload word offset >> 8)
   int32_t* num_gtiles;
+  int32_t* splits;          // [2] K splits chosen for FC1 and FC2
+  int split_cfg[2][4];      // per GEMM: column groups, K steps, most splits, launched wavefronts
   ExpertInfo* einfo;
   uint32_t packed_bits[32]; // 2 bits per expert: bits - 2
 };
@@ -57,7 +59,7 @@ struct RotateArgs {          // a = R_H(su1_e * x_t) per slot, fp16 or MXFP8
 
 struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_I(z_u)))
   const float* z;            // [splits][R][2I] unscaled partial sums
-  int splits;
+  const int32_t* splits;     // device: FC1 split count
   const void* ids;
   int ids64;
   const int32_t* sorted_routes;
@@ -73,12 +75,15 @@ struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_
 };
 
 struct CombineArgs {         // y_t = sum_j w[t,j] * sv2_e * R_H(scale2_e * v_slot)
-  const float* v;            // [splits][R][H]
-  int splits;
+  float* v;                  // [splits][R][H]; plane 0 is overwritten with the weighted rotated rows
+  const int32_t* splits;     // device: FC2 split count
   const void* ids;
   int ids64;
   const float* w;            // [T][k]
   const int32_t* route_slot;
+  const int32_t* sorted_routes;
+  const int32_t* offsets;
+  int num_experts;
   int top_k;
   int tokens;
   int routes;
@@ -97,8 +102,8 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
   float* out;                // [splits][R][N]
   const int4* gtiles;
   const int32_t* num_gtiles;
+  const int32_t* splits;     // device: split count of this GEMM
   int K, N;
-  int splits;
   int routes;                // R: row stride between split planes
 };
 
@@ -106,9 +111,10 @@ void launch_route_map(const RouteMapArgs& a, hipStream_t s);
 void launch_rotate(const RotateArgs& a, bool mx, hipStream_t s);
 void launch_act(const ActArgs& a, bool mx, hipStream_t s);
 void launch_combine(const CombineArgs& a, hipStream_t s);
+// fc: 1 or 2 (names the kernel); bits: the width shared by every expert (2, 3, 4) or 0 if mixed;
 // mg: 16-row groups per GEMM tile (1, 2 or 4); waves: persistent wave count
-void launch_gemm_f16(const GemmArgs& a, int mg, int waves, hipStream_t s);
-void launch_gemm_f8(const GemmArgs& a, int mg, int waves, hipStream_t s);
+void launch_gemm_f16(const GemmArgs& a, int fc, int bits, int mg, int waves, hipStream_t s);
+void launch_gemm_f8(const GemmArgs& a, int fc, int bits, int mg, int waves, hipStream_t s);
 
 void launch_debug_decode(const uint16_t* matrix_words, int bits, int K, int N, int as_e4m3, void* out,
                          hipStream_t s);

@@ -113,6 +113,12 @@ class Plan:
                  scratch.numel(), _stream(x.device)), "tmoe_forward_w4a8" if w4a8 else "tmoe_forward_w4a16")
         return y
 
+    def forward_stages(self, first: int, last: int, x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor,
+                       weights: DeviceWeights, scratch: torch.Tensor, y: torch.Tensor, w4a8: bool = False) -> None:
+        check(lib.tmoe_forward_stages(self.handle, int(w4a8), first, last, _ptr(x), _ptr(ids), _ptr(w), x.shape[0],
+                                      ctypes.byref(weights.c), _ptr(y), _ptr(scratch), scratch.numel(),
+                                      _stream(x.device)), "tmoe_forward_stages")
+
     def forward_status(self, x, ids, w, T, weights, y, scratch, scratch_bytes, w4a8=False, stream=None) -> int:
         """Raw status of a forward call with explicit (possibly invalid) arguments; for tests."""
         fn = lib.tmoe_forward_w4a8 if w4a8 else lib.tmoe_forward_w4a16

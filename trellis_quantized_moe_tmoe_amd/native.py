@@ -18,7 +18,8 @@ IDS_I32, IDS_I64 = 0, 1
 
 # every symbol declared in include/tmoe.h
 EXPORTS = ["tmoe_plan", "tmoe_plan_destroy", "tmoe_plan_get_info", "tmoe_plan_expert_offset",
-           "tmoe_build_route_map", "tmoe_forward_w4a16", "tmoe_forward_w4a8", "tmoe_status_str",
+           "tmoe_build_route_map", "tmoe_forward_w4a16", "tmoe_forward_w4a8", "tmoe_forward_stages",
+           "tmoe_status_str",
            "tmoe_debug_decode", "tmoe_debug_mxfp8", "tmoe_debug_rotate", "tmoe_debug_get_views"]
 
 
@@ -46,8 +47,7 @@ class PlanInfo(ctypes.Structure):
 
 
 class DebugViews(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("a1", "a1_scale", "z", "b", "b_scale", "v")] + \
-               [("splits1", ctypes.c_int32), ("splits2", ctypes.c_int32)]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("a1", "a1_scale", "z", "b", "b_scale", "v", "splits")]
 
 
 class TmoeError(RuntimeError):
@@ -57,6 +57,13 @@ class TmoeError(RuntimeError):
 
 
 def _load():
+    # torch ships its own HIP runtime library. Loading it first makes libtmoe.so bind to that same
+    # runtime (same soname), so device pointers and streams from torch are valid for our launches;
+    # loading libtmoe.so first would pull in a second runtime from the system ROCm.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
     lib = ctypes.CDLL(LIB_PATH)
@@ -69,6 +76,7 @@ def _load():
     fwd = [P, P, P, P, I32, ctypes.POINTER(Weights), P, P, SZ, P]
     lib.tmoe_forward_w4a16.argtypes = fwd
     lib.tmoe_forward_w4a8.argtypes = fwd
+    lib.tmoe_forward_stages.argtypes = [P, I32, I32, I32, P, P, P, I32, ctypes.POINTER(Weights), P, P, SZ, P]
     lib.tmoe_status_str.argtypes = [I32]
     lib.tmoe_status_str.restype = ctypes.c_char_p
     lib.tmoe_debug_decode.argtypes = [P, ctypes.POINTER(Weights), I32, I32, I32, P, P]
