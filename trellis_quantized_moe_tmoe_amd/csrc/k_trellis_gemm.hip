@@ -27,7 +27,7 @@ namespace tmoe {
 namespace {
 
 constexpr int NS = 4;   // 16-column strips per wavefront unit (64 columns)
-constexpr int DF = 4;   // fp16 path: K steps in flight
+constexpr int DF = 2;   // fp16 path: K steps in flight
 constexpr int D8 = 2;   // fp8 path: K steps in flight (each step is 4x deeper)
 
 // A wave-uniform global pointer held in scalar registers (loads through it use the global path with
@@ -155,8 +155,7 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
 // BITS = 0: experts of mixed widths, chosen per unit. FC (1 or 2) only names the instantiation,
 // so profiles tell the two GEMMs apart.
 template <int BITS, int MG, int FC>
-__global__ __launch_bounds__(256) void k_gemm_f16(GemmArgs a) {
-  __shared__ uint32_t ring_all[4 * ring_words<MG>()];  // one ring per wavefront
+__device__ __forceinline__ void gemm_f16_body(const GemmArgs& a, uint32_t* ring_all) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wv);
@@ -181,6 +180,20 @@ __global__ __launch_bounds__(256) void k_gemm_f16(GemmArgs a) {
       else unit_f16<2, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
     }
   }
+}
+
+// Decode-size tiles (16 rows): sized to keep five wavefronts per SIMD resident, so a round of
+// units covers the chip evenly.
+template <int BITS, int MG, int FC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 0 ? 3 : 5, 8))) void k_gemm_f16_small(GemmArgs a) {
+  __shared__ uint32_t ring_all[4 * ring_words<MG>()];
+  gemm_f16_body<BITS, MG, FC>(a, ring_all);
+}
+
+template <int BITS, int MG, int FC>
+__global__ __launch_bounds__(256) void k_gemm_f16(GemmArgs a) {
+  __shared__ uint32_t ring_all[4 * ring_words<MG>()];
+  gemm_f16_body<BITS, MG, FC>(a, ring_all);
 }
 
 // 32 E4M3 weights of one lane for one 128-deep K step: tiles kt0 (bytes 0-15) and kt0+4
@@ -362,7 +375,7 @@ template <int BITS, int FC>
 void launch_f16(const GemmArgs& a, int mg, dim3 grid, hipStream_t s) {
   if (mg >= 4) hipLaunchKernelGGL((k_gemm_f16<BITS, 4, FC>), grid, dim3(256), 0, s, a);
   else if (mg == 2) hipLaunchKernelGGL((k_gemm_f16<BITS, 2, FC>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_gemm_f16<BITS, 1, FC>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_gemm_f16_small<BITS, 1, FC>), grid, dim3(256), 0, s, a);
 }
 
 template <int BITS, int FC>

@@ -26,7 +26,7 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxDim = 4096;
 constexpr long long kMaxRoutes = 1LL << 24;
 constexpr size_t kAlign = 256;
-constexpr int kGemmWaveCap = 4096;
+constexpr int kGemmWaveCap = 5120;   // 256 CUs x 4 SIMDs x 5 wavefronts
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
