@@ -133,6 +133,22 @@ class Bench:
         out["enqueued_within_hold"] = bool(enqueue_s < 0.8 * hold_s)
         return out
 
+    def _kernel_ms(self, stage: int, n: int) -> float:
+        """Average duration of one stage's kernel: n launches of that stage alone (cycling the weight
+        copies, over the route map and inputs the last forward left in scratch) queued behind a
+        bounded spin kernel, between two events on the launch stream."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        hold_s = 0.05
+        torch.cuda._sleep(int(hold_s * 2.4e9))
+        e0.record()
+        for i in range(n):
+            self.stages(i, stage, stage)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
     def run(self, steps: int, warmup: int) -> dict:
         torch = self.torch
         for i in range(warmup):
@@ -141,7 +157,9 @@ class Bench:
         # headline: K steps in one graph, timed with events on the launch stream
         ms_step = self._graph_time(self.forward, steps, reps=1)
         stage_ms = self._staged_ms(steps)
-        return dict(ms_step=ms_step, stage_ms=stage_ms)
+        self.forward(0)
+        kernel_ms = {nm: self._kernel_ms(k, steps) for k, nm in enumerate(STAGES) if nm in ("fc1", "fc2")}
+        return dict(ms_step=ms_step, stage_ms=stage_ms, kernel_ms=kernel_ms)
 
 
 def cpu_baseline(inp, budget_s: float = 15.0):
@@ -176,8 +194,9 @@ def main():
     r = b.run(args.steps, args.warmup)
     ms = r["ms_step"]
     st = r["stage_ms"]
-    fc1_gbs = b.fc1_bytes / (st["fc1"] * 1e-3) / 1e9
-    fc2_gbs = b.fc2_bytes / (st["fc2"] * 1e-3) / 1e9
+    km = r["kernel_ms"]
+    fc1_gbs = b.fc1_bytes / (km["fc1"] * 1e-3) / 1e9
+    fc2_gbs = b.fc2_bytes / (km["fc2"] * 1e-3) / 1e9
     H, I = b.inp.hidden, b.inp.inter
     out = {
         "metric": "routed tokens/s per MoE layer; decode weight GB/s & prefill TFLOP/s vs peak",
@@ -198,10 +217,11 @@ def main():
                    "routes": b.inp.routes, "touched_experts": b.touched, "weight_copies": b.n_copies},
         "roofline": {"bound": "hbm", "kernel": "k_gemm_f16 (FC1)" if not b.w4a8 else "k_gemm_f8 (FC1)",
                      "achieved": fc1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fc1_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": b.fc1_bytes, "avg_launch_ms": st["fc1"]},
+                     "traffic": None, "algorithmic_bytes": b.fc1_bytes, "avg_launch_ms": km["fc1"]},
         "stage_ms": st,
+        "kernel_ms": km,
         "fc2_gbs": fc2_gbs,
-        "gemm_pair_gbs": (b.fc1_bytes + b.fc2_bytes) / ((st["fc1"] + st["fc2"]) * 1e-3) / 1e9,
+        "gemm_pair_gbs": (b.fc1_bytes + b.fc2_bytes) / ((km["fc1"] + km["fc2"]) * 1e-3) / 1e9,
     }
     y = b.y.cpu().numpy()
     if args.calibrate_copy:
@@ -224,14 +244,14 @@ def main():
         for nm, t, w8 in (("prefill", 2048, False), ("w4a8", 64, True), ("wide", 16, False), ("decode", 1, False)):
             e = Bench(nm, t, w8)
             rr = e.run(max(5, args.steps // 5), 3)
-            s2 = rr["stage_ms"]
-            gemm_s = (s2["fc1"] + s2["fc2"]) * 1e-3
+            s2, k2 = rr["stage_ms"], rr["kernel_ms"]
+            gemm_s = (k2["fc1"] + k2["fc2"]) * 1e-3
             peak = MFMA_F8_PEAK_TFLOPS if w8 else MFMA_F16_PEAK_TFLOPS
             tf = (e.flops_fc1 + e.flops_fc2) / gemm_s / 1e12
             gbs = (e.fc1_bytes + e.fc2_bytes) / gemm_s / 1e9
             extra[f"{nm}:{t}"] = {"tokens_per_s": t / (rr["ms_step"] * 1e-3), "ms_per_step": rr["ms_step"],
                                   "gemm_tflops": tf, "gemm_tflops_frac": tf / peak, "gemm_weight_gbs": gbs,
-                                  "gemm_weight_gbs_frac": gbs / HBM_PEAK_GBS, "stage_ms": s2,
+                                  "gemm_weight_gbs_frac": gbs / HBM_PEAK_GBS, "stage_ms": s2, "kernel_ms": k2,
                                   "touched_experts": e.touched, "weight_copies": e.n_copies}
             del e
             torch.cuda.empty_cache()

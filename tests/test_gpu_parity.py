@@ -124,6 +124,20 @@ def test_layer_w4a8(T):
     assert err_16 <= 0.12     # measured, not the 3e-2 target: E4M3 operands carry ~2.6% RMS each
 
 
+@pytest.mark.parametrize("over", [
+    dict(hidden=4096, inter=256, experts=24, top_k=20),    # combine: 3 wavefronts, 7 rounds over k = 20
+    dict(hidden=1024, inter=256, experts=40, top_k=32),    # combine: 14 wavefronts, 3 rounds over k = 32
+    dict(hidden=256, inter=4096, experts=4, top_k=3),      # widest activation row (64 values per lane)
+    dict(hidden=192, inter=320, experts=5, top_k=5),       # 128 + 64 blocks on both sides, k = E
+])
+def test_layer_w4a16_shape_edges(over):
+    c = Case("tiny", 4, **over)
+    y = c.run().cpu().numpy()
+    err = rel_err(y, c.oracle_w4a16)
+    say(f"[result] {c.label} W4A16 rel err {err:.3e}")
+    assert err <= TOL_W4A16
+
+
 def test_w4a16_path_on_w4a8_geometry():
     c = Case("w4a8", 32)
     err = rel_err(c.run().cpu().numpy(), c.oracle_w4a16)

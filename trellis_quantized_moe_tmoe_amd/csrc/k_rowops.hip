@@ -6,10 +6,13 @@
 //  k_act    : the activation epilogue between FC1 and FC2 in the pages' order
 //             R_I -> svh -> silu(gate) * up -> suh_down -> R_I ("integrate EXL3 Trellis into the
 //             fused W4A16 API", review of kernel.py), with the FC1 channel scales applied first.
-//  k_out_rotate + k_topk_sum: y_t = sum over j ascending of w[t,j] * sv2_e * R_H(scale2_e * v), the
-//             output rotation with exact top-k weighting. The rotation runs per route (one wavefront
-//             each), the sum per token and column in a fixed j order with no atomics, so repeated
-//             calls are bitwise identical.
+//  k_combine: y_t = sum over j ascending of w[t,j] * sv2_e * R_H(scale2_e * v), the output rotation
+//             with exact top-k weighting. One workgroup per token: each wavefront rotates one of the
+//             token's routes into LDS, then every column is summed in ascending j with no atomics,
+//             so repeated calls are bitwise identical.
+//
+// The FC1/FC2 GEMMs leave up to 8 K-split partial planes; every reader sums them in ascending split
+// order, with all loads of a row issued before the first add so one memory latency covers them.
 #include "tmoe_device.hpp"
 #include "tmoe_internal.hpp"
 
@@ -19,6 +22,40 @@ namespace {
 
 __device__ __forceinline__ long long route_expert(const void* ids, int ids64, int r) {
   return ids64 ? static_cast<const long long*>(ids)[r] : static_cast<long long>(static_cast<const int*>(ids)[r]);
+}
+
+// out[i] = sum over s < splits, ascending, of src[s * plane + 64 * i] for i < S. The host bounds
+// splits by SMAX. Planes are loaded SU at a time; when SU = SMAX the single round re-reads the last
+// plane for s >= splits (in bounds, cached) and adds it as nothing, so every load goes out before
+// the first add with no branch between them.
+template <int S, int SMAX, int SU>
+__device__ __forceinline__ void sum_splits(const float* __restrict__ src, size_t plane, int splits, float (&out)[S]) {
+#pragma unroll
+  for (int i = 0; i < S; ++i) out[i] = 0.0f;
+  auto round = [&](int s0) {
+    float t[SU][S];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int sp = s0 + u < splits ? s0 + u : splits - 1;
+#pragma unroll
+      for (int i = 0; i < S; ++i) t[u][i] = src[sp * plane + 64 * i];
+    }
+#pragma unroll
+    for (int u = 0; u < SU; ++u)
+#pragma unroll
+      for (int i = 0; i < S; ++i) out[i] += s0 + u < splits ? t[u][i] : 0.0f;
+  };
+  if constexpr (SU == SMAX) {
+    round(0);
+  } else {
+#pragma unroll 1
+    for (int s0 = 0; s0 < splits; s0 += SU) round(s0);
+  }
+}
+
+template <int S, int SMAX>
+constexpr int splits_unroll(int rows) {   // planes loaded per round: about 64 loads in flight per lane
+  return SMAX * S * rows <= 64 ? SMAX : (64 / (S * rows) >= 1 ? 64 / (S * rows) : 1);
 }
 
 // Visit the rotation blocks of a row: one power-of-two segment of EPL values per lane, or (EPL = 0)
@@ -80,7 +117,7 @@ __global__ __launch_bounds__(256) void k_rotate(RotateArgs a) {
   for_segments<EPL>(a.rot, body);
 }
 
-template <bool MX>
+template <bool MX, int SMAX>
 struct ActBody {
   const ActArgs& a;
   int lane, p, e, I, splits;
@@ -89,16 +126,14 @@ struct ActBody {
     float zg[S], zu[S];
     const size_t plane = static_cast<size_t>(a.routes) * 2 * I;
     const float* zr = a.z + static_cast<size_t>(p) * 2 * I + off + lane;
+    constexpr int SU = splits_unroll<S, SMAX>(2);
+    sum_splits<S, SMAX, SU>(zr, plane, splits, zg);
+    sum_splits<S, SMAX, SU>(zr + I, plane, splits, zu);
     const uint16_t* c1 = a.scale1 + static_cast<size_t>(e) * 2 * I + off + lane;
 #pragma unroll
     for (int i = 0; i < S; ++i) {
-      float sg = 0.0f, su = 0.0f;
-      for (int s = 0; s < splits; ++s) {
-        sg += zr[s * plane + 64 * i];
-        su += zr[s * plane + I + 64 * i];
-      }
-      zg[i] = sg * h2f(c1[64 * i]);
-      zu[i] = su * h2f(c1[I + 64 * i]);
+      zg[i] *= h2f(c1[64 * i]);
+      zu[i] *= h2f(c1[I + 64 * i]);
     }
     if (!a.rot.identity) {
       fwht_segment<S>(zg, lane);
@@ -128,72 +163,99 @@ struct ActBody {
   }
 };
 
-template <int EPL, bool MX>
+template <int EPL, bool MX, int SMAX>
 __global__ __launch_bounds__(256) void k_act(ActArgs a) {
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (p >= a.routes || p >= a.offsets[a.num_experts]) return;
   const int r = a.sorted_routes[p];
   const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
-  ActBody<MX> body{a, lane, p, e, a.rot.n, *a.splits};
+  ActBody<MX, SMAX> body{a, lane, p, e, a.rot.n, *a.splits};
   for_segments<EPL>(a.rot, body);
 }
 
-// Per route slot: o = w[r] * sv2_e * R_H(scale2_e * sum_s v_s), written over split plane 0 of the
-// same slot (each slot is read completely before it is written, by the same wavefront).
-struct OutRotBody {
+// Rotates one route's row held in LDS in place: o = wt * sv2_e * R_H(row).
+struct CombineRotBody {
   const CombineArgs& a;
-  int lane, p, e, H, splits;
+  float* row;
+  int lane, e;
   float wt;
   template <int S>
   __device__ __forceinline__ void run(int off) {
-    const size_t plane = static_cast<size_t>(a.routes) * H;
-    float* vr = a.v + static_cast<size_t>(p) * H + off + lane;
-    const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + off + lane;
     float vv[S];
 #pragma unroll
-    for (int i = 0; i < S; ++i) {
-      float acc = 0.0f;
-      for (int sp = 0; sp < splits; ++sp) acc += vr[sp * plane + 64 * i];
-      vv[i] = acc * h2f(c2[64 * i]);
-    }
+    for (int i = 0; i < S; ++i) vv[i] = row[off + 64 * i + lane];
     if (!a.rot.identity) fwht_segment<S>(vv, lane);
-    const uint16_t* sg = a.sv2 + static_cast<size_t>(e) * H + off + lane;
+    const uint16_t* sg = a.sv2 + static_cast<size_t>(e) * a.rot.n + off + lane;
 #pragma unroll
-    for (int i = 0; i < S; ++i) vr[64 * i] = wt * (vv[i] * h2f(sg[64 * i]));
+    for (int i = 0; i < S; ++i) row[off + 64 * i + lane] = wt * (vv[i] * h2f(sg[64 * i]));
   }
 };
 
-template <int EPL>
-__global__ __launch_bounds__(256) void k_out_rotate(CombineArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (p >= a.routes || p >= a.offsets[a.num_experts]) return;
-  const int r = a.sorted_routes[p];
-  const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
-  OutRotBody body{a, lane, p, e, a.rot.n, *a.splits, a.w[r]};
-  for_segments<EPL>(a.rot, body);
-}
-
-// y_t = sum over j ascending of o[slot(t, j)]; dropped routes add nothing. Four columns per thread.
-__global__ __launch_bounds__(256) void k_topk_sum(CombineArgs a) {
-  const int H4 = a.rot.n >> 2;
-  const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<long long>(a.tokens) * H4) return;
-  const int t = static_cast<int>(idx / H4), c = static_cast<int>(idx % H4);
-  const float4* o = reinterpret_cast<const float4*>(a.v);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < a.top_k; ++j) {
-    const int p = a.route_slot[t * a.top_k + j];
+// One workgroup of W wavefronts per token t. Round it handles routes j = it * W + w (wavefront w):
+// the split sum of v times scale2 is staged in the wavefront's LDS row, rotated there, weighted;
+// after a barrier every thread adds its columns of the W rows in ascending j onto a running sum
+// kept in LDS (the last round writes y instead). Dropped routes add nothing. LDS: (W + 1) * H floats
+// plus W flags.
+template <int EPL, int SMAX>
+__global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs a) {
+  extern __shared__ float lds[];
+  const int H = a.rot.n, K = a.top_k;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int t = blockIdx.x;
+  float* acc = lds;                         // [H]
+  float* rows = lds + H;                    // [W][H]
+  int* live = reinterpret_cast<int*>(rows + static_cast<size_t>(W) * H);   // [W]
+  float* row = rows + static_cast<size_t>(wv) * H;
+  const int splits = *a.splits;
+  const size_t plane = static_cast<size_t>(a.routes) * H;
+  const int rounds = (K + W - 1) / W;
+  for (int it = 0; it < rounds; ++it) {
+    const int j = it * W + wv;
+    const int r = t * K + j;
+    const int p = j < K ? a.route_slot[r] : -1;
+    if (lane == 0) live[wv] = p >= 0;
     if (p >= 0) {
-      const float4 x = o[static_cast<size_t>(p) * H4 + c];
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
+      const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
+      const float* src = a.v + static_cast<size_t>(p) * H + lane;
+      const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + lane;
+      constexpr int U = 8;
+      for (int base = 0; base < H; base += 64 * U) {
+        float sum[U];
+        if (base + 64 * U <= H) {
+          sum_splits<U, SMAX, splits_unroll<U, SMAX>(1)>(src + base, plane, splits, sum);
+#pragma unroll
+          for (int i = 0; i < U; ++i) row[base + 64 * i + lane] = sum[i] * h2f(c2[base + 64 * i]);
+        } else {
+          for (int c = base; c < H; c += 64) {
+            float one[1];
+            sum_splits<1, SMAX, SMAX>(src + c, plane, splits, one);
+            row[c + lane] = one[0] * h2f(c2[c]);
+          }
+        }
+      }
+      CombineRotBody body{a, row, lane, e, a.w[r]};
+      for_segments<EPL>(a.rot, body);
     }
+    __syncthreads();
+    const int H4 = H >> 2;
+    const bool last = it + 1 == rounds;
+    const int nw = K - it * W < W ? K - it * W : W;
+    for (int c = threadIdx.x; c < H4; c += blockDim.x) {
+      float4 s4 = it == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : reinterpret_cast<const float4*>(acc)[c];
+      for (int w = 0; w < nw; ++w) {
+        if (!live[w]) continue;
+        const float4 x = reinterpret_cast<const float4*>(rows + static_cast<size_t>(w) * H)[c];
+        s4.x += x.x;
+        s4.y += x.y;
+        s4.z += x.z;
+        s4.w += x.w;
+      }
+      if (last) reinterpret_cast<float4*>(a.y + static_cast<size_t>(t) * H)[c] = s4;
+      else reinterpret_cast<float4*>(acc)[c] = s4;
+    }
+    __syncthreads();
   }
-  reinterpret_cast<float4*>(a.y)[static_cast<size_t>(t) * H4 + c] = acc;
 }
 
 struct DebugRotateBody {
@@ -259,6 +321,28 @@ void dispatch_epl(const RowRot& rot, F&& f) {
 
 inline unsigned blocks_for(long long rows) { return static_cast<unsigned>((rows + 3) / 4); }
 
+template <class F>
+void dispatch_smax(int most, F&& f) {
+  switch (most) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    default: f(std::integral_constant<int, 8>{}); break;
+  }
+}
+
+constexpr size_t kCombineLdsBytes = 65536;
+
+// Wavefronts per combine workgroup: at most 16, at most top_k, and LDS within kCombineLdsBytes
+// (which keeps H = 4096 at 3, inside that kernel's 256-thread bound).
+int combine_waves(int hidden, int top_k) {
+  int w = kCombineLdsBytes / (4 * hidden) - 1;     // (W + 1) rows of H floats, plus W flags
+  while (w > 1 && static_cast<size_t>(w + 1) * hidden * 4 + 4 * w > kCombineLdsBytes) --w;
+  w = w < top_k ? w : top_k;
+  w = w < 16 ? w : 16;
+  return w < 1 ? 1 : w;
+}
+
 }  // namespace
 
 void launch_rotate(const RotateArgs& a, bool mx, hipStream_t s) {
@@ -271,19 +355,23 @@ void launch_rotate(const RotateArgs& a, bool mx, hipStream_t s) {
 
 void launch_act(const ActArgs& a, bool mx, hipStream_t s) {
   dispatch_epl(a.rot, [&](auto epl) {
-    constexpr int E = decltype(epl)::value;
-    if (mx) hipLaunchKernelGGL((k_act<E, true>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_act<E, false>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
+    dispatch_smax(a.max_splits, [&](auto sm) {
+      constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;
+      if (mx) hipLaunchKernelGGL((k_act<E, true, SM>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_act<E, false, SM>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
+    });
   });
 }
 
 void launch_combine(const CombineArgs& a, hipStream_t s) {
+  const int W = combine_waves(a.rot.n, a.top_k);
+  const size_t lds = static_cast<size_t>(W + 1) * a.rot.n * 4 + 4 * W;
   dispatch_epl(a.rot, [&](auto epl) {
-    constexpr int E = decltype(epl)::value;
-    hipLaunchKernelGGL((k_out_rotate<E>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
+    dispatch_smax(a.max_splits, [&](auto sm) {
+      constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;
+      hipLaunchKernelGGL((k_combine<E, SM>), dim3(a.tokens), dim3(64 * W), lds, s, a);
+    });
   });
-  const long long n = static_cast<long long>(a.tokens) * (a.rot.n / 4);
-  hipLaunchKernelGGL(k_topk_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a);
 }
 
 void launch_debug_rotate(float* data, long long rows, const RowRot& rot, hipStream_t s) {

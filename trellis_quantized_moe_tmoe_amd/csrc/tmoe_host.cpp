@@ -271,6 +271,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   ActArgs aa;
   aa.z = z;
   aa.splits = splits_dev;
+  aa.max_splits = sh[0].most;
   aa.ids = ids;
   aa.ids64 = p->ids64;
   aa.sorted_routes = sorted;
@@ -302,13 +303,11 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   CombineArgs ca;
   ca.v = v;
   ca.splits = splits_dev + 1;
+  ca.max_splits = sh[1].most;
   ca.ids = ids;
   ca.ids64 = p->ids64;
   ca.w = w;
   ca.route_slot = at<int32_t>(scratch, p->lay.slot);
-  ca.sorted_routes = sorted;
-  ca.offsets = offsets;
-  ca.num_experts = p->E;
   ca.top_k = p->K;
   ca.tokens = T;
   ca.routes = static_cast<int>(R);

@@ -60,6 +60,7 @@ struct RotateArgs {          // a = R_H(su1_e * x_t) per slot, fp16 or MXFP8
 struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_I(z_u)))
   const float* z;            // [splits][R][2I] unscaled partial sums
   const int32_t* splits;     // device: FC1 split count
+  int max_splits;            // host bound on *splits: 1, 2, 4 or 8
   const void* ids;
   int ids64;
   const int32_t* sorted_routes;
@@ -74,19 +75,17 @@ struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_
   int routes;
 };
 
-struct CombineArgs {         // y_t = sum_j w[t,j] * sv2_e * R_H(scale2_e * v_slot)
-  float* v;                  // [splits][R][H]; plane 0 is overwritten with the weighted rotated rows
+struct CombineArgs {         // y_t = sum_j w[t,j] * sv2_e * R_H(scale2_e * v_slot), j ascending
+  const float* v;            // [splits][R][H] FC2 partial sums (read only)
   const int32_t* splits;     // device: FC2 split count
+  int max_splits;            // host bound on *splits: 1, 2, 4 or 8
   const void* ids;
   int ids64;
   const float* w;            // [T][k]
-  const int32_t* route_slot;
-  const int32_t* sorted_routes;
-  const int32_t* offsets;
-  int num_experts;
+  const int32_t* route_slot; // [T][k]: slot of route (t, j), -1 if dropped
   int top_k;
   int tokens;
-  int routes;
+  int routes;                // R: row stride between split planes
   const uint16_t* scale2;    // [E][H]
   const uint16_t* sv2;       // [E][H]
   RowRot rot;                // n = H
