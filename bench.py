@@ -10,7 +10,8 @@ weight bytes come from HBM.
 Timing: the K steps are captured into one hipGraph and replayed between two events on the launch
 stream. Per-stage durations come from K more forwards issued stage by stage with events between
 the stages on the same stream, queued behind a bounded spin kernel so the GPU runs them back to
-back; the dominant kernel's average duration gives the roofline figure.
+back. The dominant kernel's average duration (for the roofline figure) comes from K back-to-back
+launches of that kernel alone between two events, also queued behind the spin kernel.
 
 Prints one JSON line.
 """
@@ -33,6 +34,9 @@ MFMA_F16_PEAK_TFLOPS = 2516.6
 MFMA_F8_PEAK_TFLOPS = 5033.2
 STAGES = ["route_map", "rotate", "fc1", "act", "fc2", "combine"]
 COPY_FOOTPRINT = 1.0e9
+# Stored FETCH_SIZE / WRITE_SIZE counters of the headline kernel and the sources they were taken with
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_f16_small_fc1_decode_T16_traffic.txt")
+TRAFFIC_SOURCES = ["k_trellis_gemm.hip", "tmoe_device.hpp", "tmoe_internal.hpp", "tmoe_host.cpp"]
 
 
 def parse():
@@ -162,6 +166,32 @@ class Bench:
         return dict(ms_step=ms_step, stage_ms=stage_ms, kernel_ms=kernel_ms)
 
 
+def stored_traffic(workload: str):
+    """HBM bytes per launch of the headline FC1 kernel from the stored counter runs: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) each scaled by what the same counter read for a 256 MiB device copy.
+    None for another workload, or when the kernel sources changed since the counters were taken."""
+    import hashlib
+    if workload != "decode:16" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "trellis_quantized_moe_tmoe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != kv.get("source_sha256"):
+        return None
+    copy = float(kv["copy_bytes"])
+    fetch = float(kv["fetch_kib_per_dispatch"]) * copy / float(kv["copy_fetch_kib"])
+    write = float(kv["write_kib_per_dispatch"]) * copy / float(kv["copy_write_kib"])
+    return {"bytes": fetch + write, "read_bytes": fetch, "write_bytes": write,
+            "fetch_scale": copy / (1024 * float(kv["copy_fetch_kib"])),
+            "write_scale": copy / (1024 * float(kv["copy_write_kib"]))}
+
+
 def cpu_baseline(inp, budget_s: float = 15.0):
     """The float64 oracle on host cores, repeated on the same workload for a bounded time."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -198,6 +228,7 @@ def main():
     fc1_gbs = b.fc1_bytes / (km["fc1"] * 1e-3) / 1e9
     fc2_gbs = b.fc2_bytes / (km["fc2"] * 1e-3) / 1e9
     H, I = b.inp.hidden, b.inp.inter
+    tr = stored_traffic(args.workload)
     out = {
         "metric": "routed tokens/s per MoE layer; decode weight GB/s & prefill TFLOP/s vs peak",
         "value": T / (ms * 1e-3),
@@ -215,9 +246,10 @@ def main():
                                f"trellis bits {sorted(set(b.inp.bits.tolist()))} "
                                f"{'W4A8' if b.w4a8 else 'W4A16'}",
                    "routes": b.inp.routes, "touched_experts": b.touched, "weight_copies": b.n_copies},
-        "roofline": {"bound": "hbm", "kernel": "k_gemm_f16 (FC1)" if not b.w4a8 else "k_gemm_f8 (FC1)",
+        "roofline": {"bound": "hbm", "kernel": "k_gemm_f16_small (FC1)" if not b.w4a8 else "k_gemm_f8 (FC1)",
                      "achieved": fc1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fc1_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": b.fc1_bytes, "avg_launch_ms": km["fc1"]},
+                     "traffic": tr["bytes"] if tr else None, "traffic_unit": "HBM bytes per launch",
+                     "traffic_detail": tr, "algorithmic_bytes": b.fc1_bytes, "avg_launch_ms": km["fc1"]},
         "stage_ms": st,
         "kernel_ms": km,
         "fc2_gbs": fc2_gbs,
