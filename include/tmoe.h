@@ -169,15 +169,17 @@ tmoe_status tmoe_debug_mxfp8(const float *in, int64_t rows, int32_t cols, uint8_
 tmoe_status tmoe_debug_rotate(float *rows_data, int64_t rows, int32_t n, void *stream);
 
 typedef struct {                 /* where a forward call leaves its intermediates, for tests */
-  void *a1;                      /* [T*k][H] fp16 (W4A16) or E4M3 bytes (W4A8), slot order      */
+  void *a1;                      /* [T*k][a1_pitch] fp16 (W4A16) or E4M3 bytes (W4A8), slot order;
+                                    the first H entries of each row are the rotated input           */
   uint8_t *a1_scale;             /* [T*k][H/32] E8M0 (W4A8)                                      */
   float *z;                      /* [splits[0]][T*k][2I] fp32 FC1 partial sums, unscaled, slot order */
-  void *b;                       /* [T*k][I] fp16 or E4M3, slot order                             */
+  void *b;                       /* [T*k][b_pitch] fp16 or E4M3, slot order (first I entries used) */
   uint8_t *b_scale;              /* [T*k][I/32] E8M0 (W4A8)                                      */
-  float *v;                      /* [splits[1]][T*k][H] fp32 FC2 partial sums, unscaled, slot order;
-                                    the combine stage overwrites plane 0 with w * sv2 * R_H(scale2 * v) */
+  float *v;                      /* [splits[1]][T*k][H] fp32 FC2 partial sums, unscaled, slot order */
   int32_t *splits;               /* device [2]: K splits of FC1 and FC2, chosen by the route-map
                                     kernel from the tile count (readable after the stream completes) */
+  int32_t a1_pitch, b_pitch;     /* row pitch of a1 and b in elements: H and I for W4A8; for W4A16
+                                    padded so that rows do not all start on the same memory channel */
 } tmoe_debug_views;
 
 /* Views of the intermediates a forward call with T tokens leaves in scratch; w4a8 names the

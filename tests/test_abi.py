@@ -135,5 +135,8 @@ def test_route_map_and_debug_validation(N):
     assert N.lib.tmoe_debug_get_views(h, 17, 0, fake, sb, ctypes.byref(v)) == 4
     assert N.lib.tmoe_debug_get_views(h, 4, 0, fake, sb, ctypes.byref(v)) == 0
     assert v.splits and v.a1 == fake + (v.a1 - fake)
+    assert v.a1_pitch >= 1024 and v.b_pitch >= 512
+    assert N.lib.tmoe_debug_get_views(h, 4, 1, fake, sb, ctypes.byref(v)) == 0
+    assert (v.a1_pitch, v.b_pitch) == (1024, 512)
     assert N.lib.tmoe_status_str(3).decode().startswith("scratch")
     N.lib.tmoe_plan_destroy(h)

@@ -93,7 +93,7 @@ struct RotateBody {
     for (int i = 0; i < S; ++i) v[i] = bf16_to_f32(xr[64 * i]) * h2f(sr[64 * i]);
     if (!a.rot.identity) fwht_segment<S>(v, lane);
     if constexpr (!MX) {
-      _Float16* out = static_cast<_Float16*>(a.a1) + static_cast<size_t>(p) * H + off + lane;
+      _Float16* out = static_cast<_Float16*>(a.a1) + static_cast<size_t>(p) * a.lda + off + lane;
 #pragma unroll
       for (int i = 0; i < S; ++i) out[64 * i] = static_cast<_Float16>(v[i]);
     } else {
@@ -151,7 +151,7 @@ struct ActBody {
     }
     if (!a.rot.identity) fwht_segment<S>(bb, lane);
     if constexpr (!MX) {
-      _Float16* out = static_cast<_Float16*>(a.b) + static_cast<size_t>(p) * I + off + lane;
+      _Float16* out = static_cast<_Float16*>(a.b) + static_cast<size_t>(p) * a.ldb + off + lane;
 #pragma unroll
       for (int i = 0; i < S; ++i) out[64 * i] = static_cast<_Float16>(bb[i]);
     } else {

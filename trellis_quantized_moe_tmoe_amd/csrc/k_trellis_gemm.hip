@@ -48,9 +48,9 @@ __device__ __forceinline__ gptr<T> uniform_ptr(const T* p) {
 // trellis words (two 16-deep tile rows x NS strips = 2*NS*TW 32-bit words, 1 KB at 4 bits; lane L
 // copies chunk L) and its A fragments (MG x 1 KB; each lane copies exactly the 16 bytes it later
 // feeds to the MFMA). The memory pipeline thus holds DF steps per wavefront without registers, and
-// the only waits are on the ring. Rows of the A fragment beyond the tile are loaded from the tile's
-// last row and their output rows are never stored (an MFMA output row depends on its own A row
-// only), so no masking sits in the K loop.
+// the only waits are on the ring. Rows of the A fragment beyond the tile are not loaded (first row
+// group) or repeat the tile's last row (later groups); their output rows are never stored (an MFMA
+// output row depends on its own A row only), so no masking sits in the MFMA chain.
 template <int MG>
 constexpr int ring_words() { return DF * (2 * NS * 32 + MG * 256); }
 
@@ -71,7 +71,7 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
   const int nt0 = ng * NS;
   const gptr<uint32_t> mat = uniform_ptr(reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS) +
                                          static_cast<size_t>(nt0) * TW);
-  const gptr<_Float16> A = uniform_ptr(static_cast<const _Float16*>(a.a) + static_cast<size_t>(row0) * a.K);
+  const gptr<_Float16> A = uniform_ptr(static_cast<const _Float16*>(a.a) + static_cast<size_t>(row0) * a.lda);
   // staging of trellis words: lane L < BW/4 copies 16-byte chunk L, [tile row][strip][chunk] order
   const bool stager = lane < BW / 4;
   const int st_tile = lane / (NS * CPT), st_strip = (lane / CPT) % NS, st_chunk = lane % CPT;
@@ -83,7 +83,12 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
   const int rd_b = (grp >> 1) * NS * TW + ((j0 + 1 == TW) ? 0 : j0 + 1);
   int aoff[MG];
 #pragma unroll
-  for (int mg = 0; mg < MG; ++mg) aoff[mg] = min(16 * mg + col, rows - 1) * a.K + 8 * grp;
+  for (int mg = 0; mg < MG; ++mg) aoff[mg] = min(16 * mg + col, rows - 1) * a.lda + 8 * grp;
+  // Lanes of the first row group whose row lies beyond the tile load nothing (lane 0's row always
+  // exists, so every step still issues the same number of load instructions and the ring's wait
+  // counts hold); their LDS bytes are stale and only feed output rows that are never stored. The
+  // other row groups load a repeat of the last row instead, as a whole group may lie beyond the tile.
+  const bool a_live = col < rows;
 
   f4 acc[MG][NS];
 #pragma unroll
@@ -99,8 +104,9 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
     const gptr<_Float16> ab = A + 32 * ks;
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg)
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(ab + aoff[mg]),
-                                       (void __attribute__((address_space(3)))*)(slot + 2 * NS * 32 + mg * 256), 16, 0, 0);
+      if (mg > 0 || a_live)
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(ab + aoff[mg]),
+                                         (void __attribute__((address_space(3)))*)(slot + 2 * NS * 32 + mg * 256), 16, 0, 0);
   };
   auto step = [&](int d, int next) {
     // the direct loads of the DF-1 younger steps may still be in flight
@@ -157,7 +163,7 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
 template <int BITS, int MG, int FC>
 __device__ __forceinline__ void gemm_f16_body(const GemmArgs& a, uint32_t* ring_all) {
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, kept in an SGPR
   const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wv);
   const int W = gridDim.x * 4;
   const int NG = a.N / (16 * NS);
@@ -194,6 +200,178 @@ template <int BITS, int MG, int FC>
 __global__ __launch_bounds__(256) void k_gemm_f16(GemmArgs a) {
   __shared__ uint32_t ring_all[4 * ring_words<MG>()];
   gemm_f16_body<BITS, MG, FC>(a, ring_all);
+}
+
+// Prefill-size tiles: one workgroup of four wavefronts computes a tile of 128 slots (one expert) x
+// 64*SPW output columns over its K range; each wavefront owns SPW adjacent 16-column strips. Each
+// 32-deep K step's operands arrive with direct global->LDS loads into a ring BIG_D steps deep: the
+// A rows of the step (shared: each wavefront copies two of the eight 16-row groups, already in the
+// MFMA A-operand order) and the trellis words of each wavefront's own strips. A wavefront decodes
+// only its own strips, so no decoded weight crosses LDS and every weight of the tile is decoded once
+// per 128 rows; each A fragment read from LDS feeds SPW MFMAs. One barrier per step publishes the A
+// rows and frees the ring slot of the step before. Every load is issued for every step (indices
+// clamped at the end of the range), so the wait counts are constants.
+constexpr int BIG_ROWS = 128;
+constexpr int BIG_D = 4;                       // ring depth in K steps (3 in flight)
+constexpr int BIG_A_U4 = 8 * 64;               // 16-byte chunks of A per step (8 KB)
+
+template <int SPW>
+constexpr int big_w_u4() { return 4 * SPW * 16; }     // trellis-word chunks per step, sized for 4 bits
+template <int SPW>
+constexpr int big_slot_u4() { return BIG_A_U4 + big_w_u4<SPW>(); }
+
+template <int BITS, int SPW>
+__device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, int nb, int s, int splits, int lane,
+                                             int wv, uint4* ring, uint32_t mask, uint32_t orv) {
+  constexpr int TW = 8 * BITS;                   // 32-bit words per tile
+  constexpr int SLOT = big_slot_u4<SPW>();
+  constexpr int RUN = SPW * TW;                  // words of one tile row of this wavefront's strips
+  const long long woff = (static_cast<long long>(static_cast<unsigned>(t.w)) << 8);
+  const int row0 = t.y, rows = t.z;
+  const int NT = a.N >> 4;
+  const int col = lane & 15, grp = lane >> 4;
+  const int q = 2 * col + (grp & 1);
+  const int ksteps = (a.K >> 5) / splits;
+  const int ks0 = s * ksteps, last = ks0 + ksteps - 1;
+  const int nt0 = (nb * 4 + wv) * SPW;                    // this wavefront's first strip
+  const gptr<uint32_t> mat = uniform_ptr(reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS) +
+                                         static_cast<size_t>(nt0) * TW);
+  const gptr<_Float16> A = uniform_ptr(static_cast<const _Float16*>(a.a) + static_cast<size_t>(row0) * a.lda);
+  // A rows copied by this wavefront: row groups 2 * wv and 2 * wv + 1, in MFMA operand order
+  int aoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) aoff[i] = min(16 * (2 * wv + i) + col, rows - 1) * a.lda + 8 * grp;
+  // trellis words: per step two tile rows x SPW adjacent tiles = two runs of RUN words; lane
+  // L < RUN / 2 copies 16-byte piece L % (RUN / 4) of run L / (RUN / 4)
+  const bool stager = lane < RUN / 2;
+  const int st_run = lane / (RUN / 4), st_piece = lane % (RUN / 4);
+  const int st_src = st_run * NT * TW + 4 * st_piece;            // words, relative to the step
+  // window words of group q in tile row (grp >> 1) of strip j: [run][strip][TW] in the slot
+  const int j0 = window_word<BITS>(q);
+  const int rd_a = (grp >> 1) * RUN + (j0 < 0 ? j0 + TW : j0);
+  const int rd_b = (grp >> 1) * RUN + ((j0 + 1 == TW) ? 0 : j0 + 1);
+
+  auto issue = [&](int ks, int slot) {
+    uint4* sl = ring + slot * SLOT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(A + 32 * ks + aoff[i]),
+                                       (void __attribute__((address_space(3)))*)(sl + (2 * wv + i) * 64), 16, 0, 0);
+    if (stager)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(mat + static_cast<size_t>(2 * ks) * NT * TW + st_src),
+                                       (void __attribute__((address_space(3)))*)(sl + BIG_A_U4 + wv * SPW * 16), 16, 0, 0);
+  };
+
+  f4 acc[8][SPW];
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) acc[g][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int d = 0; d < BIG_D - 1; ++d) issue(min(ks0 + d, last), d);
+  // The weights of step ks are decoded during step ks - 1, interleaved with its MFMAs (scheduling
+  // groups below), so the VALU work of one step overlaps the matrix work of the step before.
+  auto decode_slot = [&](int slot, half8 (&bb)[SPW]) {
+    const uint32_t* ws = reinterpret_cast<const uint32_t*>(ring + slot * SLOT + BIG_A_U4 + wv * SPW * 16);
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) bb[j] = decode8<BITS>(ws[rd_a + j * TW], ws[rd_b + j * TW], q, mask, orv);
+  };
+  half8 b0[SPW], b1[SPW];
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * (BIG_D - 2)) : "memory");   // step ks0 is in
+  decode_slot(0, b0);
+  int slot = 0;
+  // One K step: MFMAs on b (decoded during the step before) while decoding the next step into nb.
+  auto step = [&](int ks, half8 (&b)[SPW], half8 (&nb)[SPW]) {
+    // Step ks + 1 has landed (only step ks + 2's three loads may be in flight) and this wavefront's
+    // LDS reads are done; a plain barrier (no fence: a fence would also wait for the younger loads)
+    // then publishes steps ks and ks + 1 and frees the slot of step ks - 1.
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(3 * (BIG_D - 3)) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");                          // no LDS access moves above the barrier
+    const int refill = slot == 0 ? BIG_D - 1 : slot - 1;
+    issue(min(ks + BIG_D - 1, last), refill);
+    const uint4* sl = ring + slot * SLOT;
+    slot = slot + 1 == BIG_D ? 0 : slot + 1;
+    // next step's words (the slot of step ks + 1; after the last step a stale slot, decoded unused)
+    const uint32_t* wsn = reinterpret_cast<const uint32_t*>(ring + slot * SLOT + BIG_A_U4 + wv * SPW * 16);
+    uint32_t wh[SPW], wl[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      wh[j] = wsn[rd_a + j * TW];
+      wl[j] = wsn[rd_b + j * TW];
+    }
+    half8 av = *reinterpret_cast<const half8*>(sl + lane);
+    __builtin_amdgcn_sched_barrier(0);
+    // Eight pieces, kept in this order: the next A fragment's LDS read, this row group's SPW MFMAs
+    // and, spread over the pieces, one strip of the next step's decode at a time.
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const half8 an = g + 1 < 8 ? *reinterpret_cast<const half8*>(sl + (g + 1) * 64 + lane) : av;
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) acc[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[j], acc[g][j], 0, 0, 0);
+      constexpr int every = 8 / SPW;
+      if (g % every == every - 1) nb[g / every] = decode8<BITS>(wh[g / every], wl[g / every], q, mask, orv);
+      av = an;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int ks = ks0;
+  for (; ks + 1 <= last; ks += 2) {
+    step(ks, b0, b1);
+    step(ks + 1, b1, b0);
+  }
+  if (ks <= last) step(ks, b0, b1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();                                          // the next unit refills the ring
+
+  float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * g + 4 * grp + i;
+      if (r < rows) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) o[r * a.N + 16 * j] = acc[g][j][i];   // < 2^31: r < 128, N <= 8192
+      }
+    }
+}
+
+// Units (tile, 64*SPW-column block, K split) are dealt to workgroups. Workgroups are dealt to the
+// eight XCDs round-robin (workgroup b runs on XCD b mod 8), so workgroup b serves the units of tile
+// (b mod 8) + 8 * (g / upt), unit g mod upt of it, with g = b div 8 and upt the units of one tile:
+// the units of one tile run on one XCD and share its L2 copy of the tile's A rows, and consecutive
+// tiles go to different XCDs. The grid is a multiple of 8 * upt (sized on the host from an upper
+// bound on the tile count), so this is a permutation of the grid; surplus workgroups leave at once.
+template <int BITS, int SPW, int FC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPW >= 4 ? 2 : 3, 8))) void k_gemm_f16_big(GemmArgs a) {
+  __shared__ uint4 ring[BIG_D * big_slot_u4<SPW>()];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, kept in an SGPR
+  const int NB = a.N / (64 * SPW);
+  const int ntiles = *a.num_gtiles;
+  const int splits = *a.splits;
+  const int units = ntiles * NB * splits;
+  const int G = gridDim.x;
+  const int upt = NB * splits;                              // units of one tile
+  const int gi = blockIdx.x >> 3;
+  const int first = ((blockIdx.x & 7) + 8 * (gi / upt)) * upt + gi % upt;
+  const uint32_t mask = vreg_const(kMcgMask), orv = kMcgOr;
+  for (int u = first; u < units; u += G) {
+    const int s = u % splits;
+    const int rest = u / splits;
+    const int nb = rest % NB;
+    const int4 t = a.gtiles[rest / NB];
+    if constexpr (BITS != 0) {
+      unit_f16_big<BITS, SPW>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    } else {
+      const int bits = (t.x >> 24) & 0xff;
+      if (bits == 4) unit_f16_big<4, SPW>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+      else if (bits == 3) unit_f16_big<3, SPW>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+      else unit_f16_big<2, SPW>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    }
+  }
 }
 
 // 32 E4M3 weights of one lane for one 128-deep K step: tiles kt0 (bytes 0-15) and kt0+4
@@ -373,7 +551,9 @@ __global__ __launch_bounds__(256) void k_debug_decode(const uint16_t* words, int
 
 template <int BITS, int FC>
 void launch_f16(const GemmArgs& a, int mg, dim3 grid, hipStream_t s) {
-  if (mg >= 4) hipLaunchKernelGGL((k_gemm_f16<BITS, 4, FC>), grid, dim3(256), 0, s, a);
+  if (mg >= 16) hipLaunchKernelGGL((k_gemm_f16_big<BITS, 4, FC>), grid, dim3(256), 0, s, a);
+  else if (mg >= 8) hipLaunchKernelGGL((k_gemm_f16_big<BITS, 2, FC>), grid, dim3(256), 0, s, a);
+  else if (mg >= 4) hipLaunchKernelGGL((k_gemm_f16<BITS, 4, FC>), grid, dim3(256), 0, s, a);
   else if (mg == 2) hipLaunchKernelGGL((k_gemm_f16<BITS, 2, FC>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_gemm_f16_small<BITS, 1, FC>), grid, dim3(256), 0, s, a);
 }
@@ -408,7 +588,7 @@ void launch_f8_bits(const GemmArgs& a, int bits, int mg, dim3 grid, hipStream_t 
 }  // namespace
 
 void launch_gemm_f16(const GemmArgs& a, int fc, int bits, int mg, int waves, hipStream_t s) {
-  const dim3 grid((waves + 3) / 4);
+  const dim3 grid(mg >= 8 ? waves : (waves + 3) / 4);   // mg >= 8: workgroups (a multiple of 8 tiles' units)
   if (fc == 1) launch_f16_bits<1>(a, bits, mg, grid, s);
   else launch_f16_bits<2>(a, bits, mg, grid, s);
 }

@@ -26,7 +26,8 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxDim = 4096;
 constexpr long long kMaxRoutes = 1LL << 24;
 constexpr size_t kAlign = 256;
-constexpr int kGemmWaveCap = 5120;   // 256 CUs x 4 SIMDs x 5 wavefronts
+constexpr int kGemmWaveCap = 5120;     // 256 CUs x 4 SIMDs x 5 wavefronts
+constexpr int kGemmGroupCap = 1 << 20; // workgroups of a 128-row tile launch (one unit each)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
@@ -50,11 +51,23 @@ int choose_splits(long long routes, int ksteps) {
   return 1;
 }
 
-int choose_mg(long long routes, int experts) {
+// GEMM tile shape code: 1, 2, 4 = 16-row groups per wavefront tile (64 columns); 8, 16 = workgroup
+// tiles of 128 rows by 128 or 256 columns for large batches (fp16 path; `big_cols` is the widest
+// workgroup tile both output widths are multiples of, or 0).
+int choose_mg(long long routes, int experts, int big_cols) {
   if (routes <= 2LL * experts) return 1;
   if (routes <= 8LL * experts) return 2;
+  if (big_cols == 256) return 16;
+  if (big_cols == 128) return 8;
   return 4;
 }
+
+int tile_rows(int mg) { return mg >= 8 ? 128 : 16 * mg; }
+
+// Row pitch (elements) of the fp16 GEMM inputs A1 and b. A row of a power-of-two multiple of 512 bytes
+// would place the 16 rows one MFMA operand load touches on a couple of memory channels only; one
+// extra 256-byte block spreads them.
+int fp16_pitch(int k) { return (2 * k) % 512 == 0 ? k + 128 : k; }
 
 struct Layout {
   size_t einfo, counts, offsets, sorted, slot, tile_e, tile_r0, tile_rows, scalars, gtiles;
@@ -100,10 +113,10 @@ void build_layout(tmoe_plan_s* p) {
   L.tile_rows = take(4ull * p->max_tiles);
   L.scalars = take(32);                               // num_tiles, status, num_gtiles, splits[2]
   L.gtiles = take(16ull * p->max_gtiles);
-  L.a1 = take(2ull * R * p->H);                       // fp16, or E4M3 + E8M0 planes
+  L.a1 = take(2ull * R * fp16_pitch(p->H));           // fp16 (padded rows), or E4M3 + E8M0 planes
   const long long zrows = max_split_rows(R, p->H / 32, p->H / 128 > 0 ? p->H / 128 : 1);
   L.z = take(4ull * zrows * 2 * p->I);
-  L.b = take(2ull * R * p->I);
+  L.b = take(2ull * R * fp16_pitch(p->I));
   const long long vrows = max_split_rows(R, p->I / 32, p->I / 128 > 0 ? p->I / 128 : 1);
   L.v = take(4ull * vrows * p->H);
   L.total = off;
@@ -141,17 +154,32 @@ struct GemmShape {          // launch shape of one grouped GEMM
   int ng, ksteps, most, waves;
 };
 
-// Column groups, K steps, split bound and persistent wavefronts of FC1 (fc = 1) or FC2 (fc = 2).
-GemmShape gemm_shape(const tmoe_plan_s* p, long long R, int gemm_rows, bool fp8, int fc) {
+// Column groups, K steps, split bound and launch size of FC1 (fc = 1) or FC2 (fc = 2). For 16- to
+// 64-row tiles a unit is one wavefront's 64 columns and `waves` counts persistent wavefronts; for
+// 128-row tiles a unit is one workgroup's 128 columns and `waves` counts workgroups.
+GemmShape gemm_shape(const tmoe_plan_s* p, long long R, int mg, bool fp8, int fc) {
   GemmShape g;
   const int K = fc == 1 ? p->H : p->I;
   const int N = fc == 1 ? 2 * p->I : p->H;
-  g.ng = N / 64;
+  const bool big = mg >= 8;
+  const int gemm_rows = tile_rows(mg);
+  g.ng = N / (mg == 16 ? 256 : big ? 128 : 64);
   g.ksteps = K / (fp8 ? 128 : 32);
   g.most = choose_splits(R, g.ksteps);
   const long long gt_ub = std::min<long long>(R, p->E + R / gemm_rows + 1);
-  g.waves = static_cast<int>(std::min<long long>(kGemmWaveCap, gt_ub * g.ng * g.most));
+  g.waves = static_cast<int>(std::min<long long>(big ? kGemmGroupCap : kGemmWaveCap, gt_ub * g.ng * g.most));
+  if (big) {                                    // a whole number of 8-tile rounds of units
+    const int per = 8 * g.ng * g.most;
+    g.waves = (g.waves + per - 1) / per * per;
+  }
   return g;
+}
+
+int big_cols(const tmoe_plan_s* p, bool fp8) {
+  if (fp8) return 0;
+  for (int c : {256, 128})
+    if (p->H % c == 0 && (2 * p->I) % c == 0) return c;
+  return 0;
 }
 
 void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_rows, const GemmShape (&sh)[2],
@@ -216,9 +244,9 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const long long R = static_cast<long long>(T) * p->K;
-  const int mg = choose_mg(R, p->E);
-  const int gemm_rows = 16 * mg;
-  const GemmShape sh[2] = {gemm_shape(p, R, gemm_rows, fp8, 1), gemm_shape(p, R, gemm_rows, fp8, 2)};
+  const int mg = choose_mg(R, p->E, big_cols(p, fp8));
+  const int gemm_rows = tile_rows(mg);
+  const GemmShape sh[2] = {gemm_shape(p, R, mg, fp8, 1), gemm_shape(p, R, mg, fp8, 2)};
   int32_t* splits_dev = at<int32_t>(scratch, p->lay.scalars) + 3;
 
   (void)hipGetLastError();   // clear a stale error so the check below reports this call only
@@ -246,6 +274,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   ra.rot = make_rot(p->H, p->rotation == TMOE_ROT_IDENTITY);
   ra.a1 = a1;
   ra.a1_scale = a1s;
+  ra.lda = fp16_pitch(p->H);
   ra.routes = static_cast<int>(R);
   if (on(1)) launch_rotate(ra, fp8, s);
 
@@ -260,6 +289,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g1.num_gtiles = at<int32_t>(scratch, p->lay.scalars) + 2;
   g1.K = p->H;
   g1.N = 2 * p->I;
+  g1.lda = fp16_pitch(p->H);
   g1.splits = splits_dev;
   g1.routes = static_cast<int>(R);
   const int waves1 = sh[0].waves;
@@ -283,6 +313,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   aa.rot = make_rot(p->I, p->rotation == TMOE_ROT_IDENTITY);
   aa.b = bq;
   aa.b_scale = bs;
+  aa.ldb = fp16_pitch(p->I);
   aa.routes = static_cast<int>(R);
   if (on(3)) launch_act(aa, fp8, s);
 
@@ -293,6 +324,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g2.out = v;
   g2.K = p->I;
   g2.N = p->H;
+  g2.lda = fp16_pitch(p->I);
   g2.splits = splits_dev + 1;
   const int waves2 = sh[1].waves;
   if (on(4)) {
@@ -404,8 +436,9 @@ tmoe_status tmoe_build_route_map(tmoe_plan_t p, const void* ids, int32_t T, void
   if (!view) return TMOE_ERR_INVALID_ARG;
   if (T == 0) return TMOE_OK;
   const long long R = static_cast<long long>(T) * p->K;
-  const int gemm_rows = 16 * choose_mg(R, p->E);
-  const GemmShape sh[2] = {gemm_shape(p, R, gemm_rows, false, 1), gemm_shape(p, R, gemm_rows, false, 2)};
+  const int mg = choose_mg(R, p->E, big_cols(p, false));
+  const int gemm_rows = tile_rows(mg);
+  const GemmShape sh[2] = {gemm_shape(p, R, mg, false, 1), gemm_shape(p, R, mg, false, 2)};
   (void)hipGetLastError();
   enqueue_route_map(p, ids, T, gemm_rows, sh, scratch, static_cast<hipStream_t>(stream));
   *view = make_view(p, scratch);
@@ -490,6 +523,8 @@ tmoe_status tmoe_debug_get_views(tmoe_plan_t p, int32_t T, int32_t w4a8, void* s
   out->b_scale = at<uint8_t>(scratch, p->lay.b) + static_cast<size_t>(R) * p->I;
   out->v = at<float>(scratch, p->lay.v);
   out->splits = at<int32_t>(scratch, p->lay.scalars) + 3;
+  out->a1_pitch = w4a8 ? p->H : fp16_pitch(p->H);
+  out->b_pitch = w4a8 ? p->I : fp16_pitch(p->I);
   return TMOE_OK;
 }
 

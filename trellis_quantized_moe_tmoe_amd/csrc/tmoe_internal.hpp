@@ -52,8 +52,9 @@ struct RotateArgs {          // a = R_H(su1_e * x_t) per slot, fp16 or MXFP8
   int num_experts;
   const uint16_t* su1;       // [E][H]
   RowRot rot;
-  void* a1;                  // fp16 [R][H] or e4m3 [R][H]
+  void* a1;                  // fp16 [R][lda] or e4m3 [R][H]
   uint8_t* a1_scale;         // [R][H/32]
+  int lda;                   // fp16 row pitch in elements (>= H)
   int routes;
 };
 
@@ -70,8 +71,9 @@ struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_
   const uint16_t* sv1;       // [E][2I]
   const uint16_t* su2;       // [E][I]
   RowRot rot;                // n = I
-  void* b;                   // fp16 [R][I] or e4m3 [R][I]
+  void* b;                   // fp16 [R][ldb] or e4m3 [R][I]
   uint8_t* b_scale;          // [R][I/32]
+  int ldb;                   // fp16 row pitch in elements (>= I)
   int routes;
 };
 
@@ -96,13 +98,14 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
   const uint16_t* payload;
   const ExpertInfo* einfo;
   long long fc2_words_per_bit;  // FC2 region starts after H*2I*bits/16 words: pass H*2I/16 or 0
-  const void* a;             // fp16 [R][K] or e4m3 [R][K]
+  const void* a;             // fp16 [R][lda] or e4m3 [R][K]
   const uint8_t* a_scale;    // [R][K/32] (fp8 only)
   float* out;                // [splits][R][N]
   const int4* gtiles;
   const int32_t* num_gtiles;
   const int32_t* splits;     // device: split count of this GEMM
   int K, N;
+  int lda;                   // fp16 A row pitch in elements (the fp8 kernels use K)
   int routes;                // R: row stride between split planes
 };
 

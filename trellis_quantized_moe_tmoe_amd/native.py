@@ -47,7 +47,8 @@ class PlanInfo(ctypes.Structure):
 
 
 class DebugViews(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("a1", "a1_scale", "z", "b", "b_scale", "v", "splits")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("a1", "a1_scale", "z", "b", "b_scale", "v", "splits")] + \
+               [("a1_pitch", ctypes.c_int32), ("b_pitch", ctypes.c_int32)]
 
 
 class TmoeError(RuntimeError):
