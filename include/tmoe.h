@@ -176,8 +176,8 @@ typedef struct {                 /* where a forward call leaves its intermediate
   void *b;                       /* [T*k][b_pitch] fp16 or E4M3, slot order (first I entries used) */
   uint8_t *b_scale;              /* [T*k][I/32] E8M0 (W4A8)                                      */
   float *v;                      /* [splits[1]][T*k][H] fp32 FC2 partial sums, unscaled, slot order */
-  int32_t *splits;               /* device [2]: K splits of FC1 and FC2, chosen by the route-map
-                                    kernel from the tile count (readable after the stream completes) */
+  int32_t *splits;               /* device [2]: K splits of FC1 and FC2 that the call used (the plan's
+                                    choice for T; readable after the stream completes)             */
   int32_t a1_pitch, b_pitch;     /* row pitch of a1 and b in elements: H and I for W4A8; for W4A16
                                     padded so that rows do not all start on the same memory channel */
 } tmoe_debug_views;

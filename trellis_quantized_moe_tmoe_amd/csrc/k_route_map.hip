@@ -21,31 +21,42 @@ namespace {
 constexpr int kWaves = 16;           // 1024 threads
 constexpr int kMaxExperts = 512;
 
-// Exclusive scan over the workgroup (one value per thread); total returned in *total.
-__device__ int block_exclusive_scan(int v, int* smem, int* total) {
+// Exclusive scans of four values per thread over the workgroup at once; totals returned in *total.
+__device__ int4 block_exclusive_scan4(int4 v, int4* smem, int4* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
+  int4 x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
+    const int y0 = __shfl_up(x.x, d, 64), y1 = __shfl_up(x.y, d, 64);
+    const int y2 = __shfl_up(x.z, d, 64), y3 = __shfl_up(x.w, d, 64);
+    if (lane >= d) {
+      x.x += y0;
+      x.y += y1;
+      x.z += y2;
+      x.w += y3;
+    }
   }
   if (lane == 63) smem[w] = x;
   __syncthreads();
   if (w == 0) {
-    int s = lane < kWaves ? smem[lane] : 0;
+    int4 s = lane < kWaves ? smem[lane] : make_int4(0, 0, 0, 0);
 #pragma unroll
     for (int d = 1; d < kWaves; d <<= 1) {
-      const int y = __shfl_up(s, d, 64);
-      if (lane >= d) s += y;
+      const int y0 = __shfl_up(s.x, d, 64), y1 = __shfl_up(s.y, d, 64);
+      const int y2 = __shfl_up(s.z, d, 64), y3 = __shfl_up(s.w, d, 64);
+      if (lane >= d) {
+        s.x += y0;
+        s.y += y1;
+        s.z += y2;
+        s.w += y3;
+      }
     }
     if (lane < kWaves) smem[lane] = s;
   }
   __syncthreads();
-  const int prefix = w > 0 ? smem[w - 1] : 0;
+  const int4 prefix = w > 0 ? smem[w - 1] : make_int4(0, 0, 0, 0);
   *total = smem[kWaves - 1];
-  __syncthreads();
-  return prefix + x - v;
+  return make_int4(prefix.x + x.x - v.x, prefix.y + x.y - v.y, prefix.z + x.z - v.z, prefix.w + x.w - v.w);
 }
 
 __device__ __forceinline__ long long load_id(const void* ids, int ids64, int r) {
@@ -67,7 +78,7 @@ __device__ __forceinline__ unsigned long long same_key_mask(int key, int nbits, 
 
 __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
   __shared__ int cnt[kWaves * kMaxExperts];   // per wave, per expert: count, then running slot
-  __shared__ int scan_smem[kWaves];
+  __shared__ int4 scan_smem[kWaves];
   __shared__ int bad_w[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int E = a.num_experts, R = a.routes;
@@ -80,13 +91,20 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
   const int beg = w * seg, end = min(R, beg + seg);
   const unsigned long long lt = (1ull << lane) - 1ull;
 
-  // pass 1: per-wave per-expert counts
-  for (int base = beg; base < end; base += 64) {
+  // pass 1: per-wave per-expert counts. The keys of a wave's first kKeep chunks stay in registers
+  // for pass 2; later chunks are read again.
+  constexpr int kKeep = 4;
+  int kept[kKeep];
+  int ci = 0;
+  for (int base = beg; base < end; base += 64, ++ci) {
     const int r = base + lane;
     const bool act = r < end;
     const long long id = act ? load_id(a.ids, a.ids64, r) : -1;
     const bool valid = act && id >= 0 && id < E;
     const int key = valid ? static_cast<int>(id) : E;
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k)
+      if (ci == k) kept[k] = key;
     const unsigned long long active = __ballot(act);
     const unsigned long long m = same_key_mask(key, nbits, active);
     const bool leader = act && ((m >> lane) == 1ull);        // highest lane of its key group
@@ -105,13 +123,13 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
     for (int ww = 0; ww < kWaves; ++ww) total_e += cnt[ww * E + tid];
     bits_e = static_cast<int>((a.packed_bits[tid >> 4] >> (2 * (tid & 15))) & 3u) + 2;
   }
-  int n_valid = 0, n_tiles = 0, n_gtiles = 0, bit_units = 0;
   const int tiles_e = own ? (total_e + a.block_m - 1) / a.block_m : 0;
   const int gtiles_e = own ? (total_e + a.gemm_rows - 1) / a.gemm_rows : 0;
-  const int off_e = block_exclusive_scan(own ? total_e : 0, scan_smem, &n_valid);
-  const int toff_e = block_exclusive_scan(tiles_e, scan_smem, &n_tiles);
-  const int goff_e = block_exclusive_scan(gtiles_e, scan_smem, &n_gtiles);
-  const int boff_e = block_exclusive_scan(own ? bits_e : 0, scan_smem, &bit_units);
+  int4 totals;
+  const int4 offs = block_exclusive_scan4(make_int4(own ? total_e : 0, tiles_e, gtiles_e, own ? bits_e : 0),
+                                          scan_smem, &totals);
+  const int off_e = offs.x, toff_e = offs.y, goff_e = offs.z, boff_e = offs.w;
+  const int n_valid = totals.x, n_tiles = totals.y, n_gtiles = totals.z;
   if (own) {
     int acc = off_e;
     for (int ww = 0; ww < kWaves; ++ww) {
@@ -144,8 +162,8 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
     a.offsets[E] = n_valid;
     *a.num_tiles = n_tiles;
     *a.num_gtiles = n_gtiles;
-    for (int f = 0; f < 2; ++f)
-      a.splits[f] = gemm_splits(n_gtiles, a.split_cfg[f][0], a.split_cfg[f][1], a.split_cfg[f][2], a.split_cfg[f][3]);
+    a.splits[0] = a.nsplit[0];
+    a.splits[1] = a.nsplit[1];
     int bad = 0;
     for (int ww = 0; ww < kWaves; ++ww) bad += bad_w[ww];
     *a.status = bad;
@@ -153,17 +171,26 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
   __syncthreads();
 
   // pass 2: stable placement, chunk by chunk in route order within each wave's segment
-  for (int base = beg; base < end; base += 64) {
+  ci = 0;
+  for (int base = beg; base < end; base += 64, ++ci) {
     const int r = base + lane;
     const bool act = r < end;
-    const long long id = act ? load_id(a.ids, a.ids64, r) : -1;
-    const bool valid = act && id >= 0 && id < E;
-    const int key = valid ? static_cast<int>(id) : E;
+    int key = E;
+    if (ci < kKeep) {
+#pragma unroll
+      for (int k = 0; k < kKeep; ++k)
+        if (ci == k) key = kept[k];
+    } else {
+      const long long id = act ? load_id(a.ids, a.ids64, r) : -1;
+      key = act && id >= 0 && id < E ? static_cast<int>(id) : E;
+    }
+    const bool valid = act && key < E;
     const unsigned long long active = __ballot(act);
     const unsigned long long m = same_key_mask(key, nbits, active);
     if (valid) {
       const int pos = cnt[w * E + key] + __popcll(m & lt);
       a.sorted_routes[pos] = r;
+      a.slot_expert[pos] = key;
       a.route_slot[r] = pos;
     } else if (act) {
       a.route_slot[r] = -1;

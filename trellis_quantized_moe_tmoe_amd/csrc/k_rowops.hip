@@ -24,10 +24,10 @@ __device__ __forceinline__ long long route_expert(const void* ids, int ids64, in
   return ids64 ? static_cast<const long long*>(ids)[r] : static_cast<long long>(static_cast<const int*>(ids)[r]);
 }
 
-// out[i] = sum over s < splits, ascending, of src[s * plane + 64 * i] for i < S. The host bounds
-// splits by SMAX. Planes are loaded SU at a time; when SU = SMAX the single round re-reads the last
-// plane for s >= splits (in bounds, cached) and adds it as nothing, so every load goes out before
-// the first add with no branch between them.
+// out[i] = sum over s < splits, ascending, of src[s * plane + 64 * i] for i < S, with splits <= SMAX
+// (the kernels here pass splits = SMAX, the host's split count). Planes are loaded SU at a time;
+// when SU = SMAX the single round re-reads the last plane for s >= splits (in bounds, cached) and
+// adds it as nothing, so every load goes out before the first add with no branch between them.
 template <int S, int SMAX, int SU>
 __device__ __forceinline__ void sum_splits(const float* __restrict__ src, size_t plane, int splits, float (&out)[S]) {
 #pragma unroll
@@ -110,9 +110,8 @@ __global__ __launch_bounds__(256) void k_rotate(RotateArgs a) {
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (p >= a.routes || p >= a.offsets[a.num_experts]) return;   // whole wavefront leaves together
-  const int r = a.sorted_routes[p];
-  const int t = r / a.top_k;
-  const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
+  const int t = a.sorted_routes[p] / a.top_k;
+  const int e = a.slot_expert[p];
   RotateBody<MX> body{a, lane, p, t, e, a.rot.n};
   for_segments<EPL>(a.rot, body);
 }
@@ -168,9 +167,8 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (p >= a.routes || p >= a.offsets[a.num_experts]) return;
-  const int r = a.sorted_routes[p];
-  const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
-  ActBody<MX, SMAX> body{a, lane, p, e, a.rot.n, *a.splits};
+  const int e = a.slot_expert[p];
+  ActBody<MX, SMAX> body{a, lane, p, e, a.rot.n, SMAX};
   for_segments<EPL>(a.rot, body);
 }
 
@@ -207,7 +205,7 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
   float* rows = lds + H;                    // [W][H]
   int* live = reinterpret_cast<int*>(rows + static_cast<size_t>(W) * H);   // [W]
   float* row = rows + static_cast<size_t>(wv) * H;
-  const int splits = *a.splits;
+  const int splits = SMAX;
   const size_t plane = static_cast<size_t>(a.routes) * H;
   const int rounds = (K + W - 1) / W;
   for (int it = 0; it < rounds; ++it) {
@@ -355,7 +353,7 @@ void launch_rotate(const RotateArgs& a, bool mx, hipStream_t s) {
 
 void launch_act(const ActArgs& a, bool mx, hipStream_t s) {
   dispatch_epl(a.rot, [&](auto epl) {
-    dispatch_smax(a.max_splits, [&](auto sm) {
+    dispatch_smax(a.nsplit, [&](auto sm) {
       constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;
       if (mx) hipLaunchKernelGGL((k_act<E, true, SM>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
       else hipLaunchKernelGGL((k_act<E, false, SM>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
@@ -367,7 +365,7 @@ void launch_combine(const CombineArgs& a, hipStream_t s) {
   const int W = combine_waves(a.rot.n, a.top_k);
   const size_t lds = static_cast<size_t>(W + 1) * a.rot.n * 4 + 4 * W;
   dispatch_epl(a.rot, [&](auto epl) {
-    dispatch_smax(a.max_splits, [&](auto sm) {
+    dispatch_smax(a.nsplit, [&](auto sm) {
       constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;
       hipLaunchKernelGGL((k_combine<E, SM>), dim3(a.tokens), dim3(64 * W), lds, s, a);
     });

@@ -168,7 +168,7 @@ __device__ __forceinline__ void gemm_f16_body(const GemmArgs& a, uint32_t* ring_
   const int W = gridDim.x * 4;
   const int NG = a.N / (16 * NS);
   const int ntiles = *a.num_gtiles;
-  const int splits = *a.splits;
+  const int splits = a.nsplit;
   const int units = ntiles * NG * splits;
   uint32_t* ring = ring_all + wv * ring_words<MG>();
   const uint32_t mask = vreg_const(kMcgMask), orv = kMcgOr;
@@ -211,7 +211,6 @@ __global__ __launch_bounds__(256) void k_gemm_f16(GemmArgs a) {
 // per 128 rows; each A fragment read from LDS feeds SPW MFMAs. One barrier per step publishes the A
 // rows and frees the ring slot of the step before. Every load is issued for every step (indices
 // clamped at the end of the range), so the wait counts are constants.
-constexpr int BIG_ROWS = 128;
 constexpr int BIG_D = 4;                       // ring depth in K steps (3 in flight)
 constexpr int BIG_A_U4 = 8 * 64;               // 16-byte chunks of A per step (8 KB)
 
@@ -351,7 +350,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPW >= 4 ? 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, kept in an SGPR
   const int NB = a.N / (64 * SPW);
   const int ntiles = *a.num_gtiles;
-  const int splits = *a.splits;
+  const int splits = a.nsplit;
   const int units = ntiles * NB * splits;
   const int G = gridDim.x;
   const int upt = NB * splits;                              // units of one tile
@@ -493,7 +492,7 @@ __global__ __launch_bounds__(256) void k_gemm_f8(GemmArgs a) {
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int W = gridDim.x * 4;
   const int NG = a.N / (16 * NS);
-  const int splits = *a.splits;
+  const int splits = a.nsplit;
   const int units = *a.num_gtiles * NG * splits;
   const uint32_t mask = vreg_const(kMcgMask), orv = kMcgOr;
   for (int u = gw; u < units; u += W) {

@@ -170,18 +170,6 @@ __device__ __forceinline__ uint32_t fp8x4_from_pairs(uint32_t pa, uint32_t pb) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// ------------------------------------------------------------------ work split
-// K splits of a grouped GEMM with `ntiles` route tiles and `ng` column groups: as many as keep the
-// unit count within the launched wavefronts (one round of units, no second-round tail), at most
-// `most`, and dividing the K steps so every split has the same depth.
-__device__ __forceinline__ int gemm_splits(int ntiles, int ng, int ksteps, int most, int waves) {
-  int s = 1;
-  const long long per_split = static_cast<long long>(ntiles) * ng;
-  while (2 * s <= most && per_split * 2 * s <= waves) s *= 2;
-  while (s > 1 && ksteps % s) s >>= 1;
-  return s;
-}
-
 // ------------------------------------------------------------------ conversions
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -70,7 +70,7 @@ int tile_rows(int mg) { return mg >= 8 ? 128 : 16 * mg; }
 int fp16_pitch(int k) { return (2 * k) % 512 == 0 ? k + 128 : k; }
 
 struct Layout {
-  size_t einfo, counts, offsets, sorted, slot, tile_e, tile_r0, tile_rows, scalars, gtiles;
+  size_t einfo, counts, offsets, sorted, slot_e, slot, tile_e, tile_r0, tile_rows, scalars, gtiles;
   size_t a1, z, b, v, total;
 };
 
@@ -107,6 +107,7 @@ void build_layout(tmoe_plan_s* p) {
   L.counts = take(4ull * p->E);
   L.offsets = take(4ull * (p->E + 1));
   L.sorted = take(4ull * R);
+  L.slot_e = take(4ull * R);
   L.slot = take(4ull * R);
   L.tile_e = take(4ull * p->max_tiles);
   L.tile_r0 = take(4ull * p->max_tiles);
@@ -204,12 +205,9 @@ void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_ro
   a.status = at<int32_t>(scratch, p->lay.scalars) + 1;
   a.num_gtiles = at<int32_t>(scratch, p->lay.scalars) + 2;
   a.splits = at<int32_t>(scratch, p->lay.scalars) + 3;
-  for (int f = 0; f < 2; ++f) {
-    a.split_cfg[f][0] = sh[f].ng;
-    a.split_cfg[f][1] = sh[f].ksteps;
-    a.split_cfg[f][2] = sh[f].most;
-    a.split_cfg[f][3] = sh[f].waves;
-  }
+  a.nsplit[0] = sh[0].most;
+  a.nsplit[1] = sh[1].most;
+  a.slot_expert = at<int32_t>(scratch, p->lay.slot_e);
   a.gtiles = at<int4>(scratch, p->lay.gtiles);
   a.einfo = at<ExpertInfo>(scratch, p->lay.einfo);
   std::memcpy(a.packed_bits, p->packed_bits, sizeof(a.packed_bits));
@@ -247,13 +245,13 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   const int mg = choose_mg(R, p->E, big_cols(p, fp8));
   const int gemm_rows = tile_rows(mg);
   const GemmShape sh[2] = {gemm_shape(p, R, mg, fp8, 1), gemm_shape(p, R, mg, fp8, 2)};
-  int32_t* splits_dev = at<int32_t>(scratch, p->lay.scalars) + 3;
 
   (void)hipGetLastError();   // clear a stale error so the check below reports this call only
   auto on = [&](int stage) { return first <= stage && stage <= last; };
   if (on(0)) enqueue_route_map(p, ids, T, gemm_rows, sh, scratch, s);
 
   const int32_t* sorted = at<int32_t>(scratch, p->lay.sorted);
+  const int32_t* slot_expert = at<int32_t>(scratch, p->lay.slot_e);
   const int32_t* offsets = at<int32_t>(scratch, p->lay.offsets);
   uint8_t* a1 = at<uint8_t>(scratch, p->lay.a1);
   uint8_t* a1s = a1 + static_cast<size_t>(R) * p->H;
@@ -264,10 +262,9 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
 
   RotateArgs ra;
   ra.x = static_cast<const uint16_t*>(x);
-  ra.ids = ids;
-  ra.ids64 = p->ids64;
   ra.top_k = p->K;
   ra.sorted_routes = sorted;
+  ra.slot_expert = slot_expert;
   ra.offsets = offsets;
   ra.num_experts = p->E;
   ra.su1 = wt->su1;
@@ -290,7 +287,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g1.K = p->H;
   g1.N = 2 * p->I;
   g1.lda = fp16_pitch(p->H);
-  g1.splits = splits_dev;
+  g1.nsplit = sh[0].most;
   g1.routes = static_cast<int>(R);
   const int waves1 = sh[0].waves;
   if (on(2)) {
@@ -300,11 +297,8 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
 
   ActArgs aa;
   aa.z = z;
-  aa.splits = splits_dev;
-  aa.max_splits = sh[0].most;
-  aa.ids = ids;
-  aa.ids64 = p->ids64;
-  aa.sorted_routes = sorted;
+  aa.nsplit = sh[0].most;
+  aa.slot_expert = slot_expert;
   aa.offsets = offsets;
   aa.num_experts = p->E;
   aa.scale1 = wt->scale1;
@@ -325,7 +319,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g2.K = p->I;
   g2.N = p->H;
   g2.lda = fp16_pitch(p->I);
-  g2.splits = splits_dev + 1;
+  g2.nsplit = sh[1].most;
   const int waves2 = sh[1].waves;
   if (on(4)) {
     if (fp8) launch_gemm_f8(g2, 2, p->uniform_bits, mg, waves2, s);
@@ -334,8 +328,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
 
   CombineArgs ca;
   ca.v = v;
-  ca.splits = splits_dev + 1;
-  ca.max_splits = sh[1].most;
+  ca.nsplit = sh[1].most;
   ca.ids = ids;
   ca.ids64 = p->ids64;
   ca.w = w;

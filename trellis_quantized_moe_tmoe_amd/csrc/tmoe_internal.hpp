@@ -26,8 +26,9 @@ struct RouteMapArgs {
   int32_t* status;
   int4* gtiles;             // (expert | bits << 24, first slot, rows, payload word offset >> 8)
   int32_t* num_gtiles;
-  int32_t* splits;          // [2] K splits chosen for FC1 and FC2
-  int split_cfg[2][4];      // per GEMM: column groups, K steps, most splits, launched wavefronts
+  int32_t* splits;          // [2] K splits of FC1 and FC2, published for the consumers and tests
+  int nsplit[2];            // the host's split counts
+  int32_t* slot_expert;     // [R]: expert of each slot
   ExpertInfo* einfo;
   uint32_t packed_bits[32]; // 2 bits per expert: bits - 2
 };
@@ -44,10 +45,9 @@ struct RowRot {
 
 struct RotateArgs {          // a = R_H(su1_e * x_t) per slot, fp16 or MXFP8
   const uint16_t* x;         // bf16 [T][H]
-  const void* ids;
-  int ids64;
   int top_k;
   const int32_t* sorted_routes;
+  const int32_t* slot_expert;
   const int32_t* offsets;    // offsets[E] = valid slots
   int num_experts;
   const uint16_t* su1;       // [E][H]
@@ -59,12 +59,9 @@ struct RotateArgs {          // a = R_H(su1_e * x_t) per slot, fp16 or MXFP8
 };
 
 struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_I(z_u)))
-  const float* z;            // [splits][R][2I] unscaled partial sums
-  const int32_t* splits;     // device: FC1 split count
-  int max_splits;            // host bound on *splits: 1, 2, 4 or 8
-  const void* ids;
-  int ids64;
-  const int32_t* sorted_routes;
+  const float* z;            // [nsplit][R][2I] unscaled partial sums
+  int nsplit;                // FC1 K splits: 1, 2, 4 or 8
+  const int32_t* slot_expert;
   const int32_t* offsets;
   int num_experts;
   const uint16_t* scale1;    // [E][2I]
@@ -78,9 +75,8 @@ struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_
 };
 
 struct CombineArgs {         // y_t = sum_j w[t,j] * sv2_e * R_H(scale2_e * v_slot), j ascending
-  const float* v;            // [splits][R][H] FC2 partial sums (read only)
-  const int32_t* splits;     // device: FC2 split count
-  int max_splits;            // host bound on *splits: 1, 2, 4 or 8
+  const float* v;            // [nsplit][R][H] FC2 partial sums (read only)
+  int nsplit;                // FC2 K splits: 1, 2, 4 or 8
   const void* ids;
   int ids64;
   const float* w;            // [T][k]
@@ -103,7 +99,7 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
   float* out;                // [splits][R][N]
   const int4* gtiles;
   const int32_t* num_gtiles;
-  const int32_t* splits;     // device: split count of this GEMM
+  int nsplit;                // K splits of this GEMM (the host's choice, also published in splits[])
   int K, N;
   int lda;                   // fp16 A row pitch in elements (the fp8 kernels use K)
   int routes;                // R: row stride between split planes
