@@ -41,16 +41,17 @@ def test_route_map_bit_exact(name, T, ids_dtype):
     _check_route_map(_route_map_host(c, view), O.route_map(c.inp.ids, c.inp.experts, view.block_m))
 
 
+@pytest.mark.parametrize("tokens", [300, 700])       # 2400 routes: one workgroup; 5600: per-chunk workgroups
 @pytest.mark.parametrize("block_m", [8, 16, 32, 48, 64])
-def test_route_map_block_sizes_and_invalid_ids(block_m):
+def test_route_map_block_sizes_and_invalid_ids(block_m, tokens):
     from trellis_quantized_moe_tmoe_amd import layer as L
     from trellis_quantized_moe_tmoe_amd.workloads import make_inputs
-    inp = make_inputs("prefill", tokens=700)
+    inp = make_inputs("prefill", tokens=tokens)
     ids = inp.ids.copy()
     rng = np.random.default_rng(block_m)
     bad = rng.random(ids.shape) < 0.03
     ids[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, inp.experts + 5)
-    say(f"[case] route map prefill T=700 block_m={block_m} invalid={int(bad.sum())}")
+    say(f"[case] route map prefill T={tokens} block_m={block_m} invalid={int(bad.sum())}")
     plan = L.Plan.for_inputs(inp, block_m=block_m)
     scratch = plan.alloc_scratch()
     dids = torch.from_numpy(ids).cuda()

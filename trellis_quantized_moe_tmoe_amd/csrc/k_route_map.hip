@@ -56,6 +56,7 @@ __device__ int4 block_exclusive_scan4(int4 v, int4* smem, int4* total) {
   __syncthreads();
   const int4 prefix = w > 0 ? smem[w - 1] : make_int4(0, 0, 0, 0);
   *total = smem[kWaves - 1];
+  __syncthreads();                               // smem may be reused after this
   return make_int4(prefix.x + x.x - v.x, prefix.y + x.y - v.y, prefix.z + x.z - v.z, prefix.w + x.w - v.w);
 }
 
@@ -76,25 +77,13 @@ __device__ __forceinline__ unsigned long long same_key_mask(int key, int nbits, 
 
 }  // namespace
 
-__global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
-  __shared__ int cnt[kWaves * kMaxExperts];   // per wave, per expert: count, then running slot
-  __shared__ int4 scan_smem[kWaves];
-  __shared__ int bad_w[kWaves];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int E = a.num_experts, R = a.routes;
-  for (int i = tid; i < kWaves * E; i += 1024) cnt[i] = 0;
-  if (tid < kWaves) bad_w[tid] = 0;
-  __syncthreads();
+// Counts of one wave's segment [beg, end) per expert into cnt[w * E + key] (invalid ids into
+// *bad). The keys of the first kKeep 64-route chunks are returned in kept[] for the placement pass.
+constexpr int kKeep = 4;
 
-  const int nbits = 32 - __clz(E);              // keys 0..E (E marks an invalid id)
-  const int seg = (R + kWaves - 1) / kWaves;
-  const int beg = w * seg, end = min(R, beg + seg);
-  const unsigned long long lt = (1ull << lane) - 1ull;
-
-  // pass 1: per-wave per-expert counts. The keys of a wave's first kKeep chunks stay in registers
-  // for pass 2; later chunks are read again.
-  constexpr int kKeep = 4;
-  int kept[kKeep];
+__device__ __forceinline__ void count_segment(const RouteMapArgs& a, int beg, int end, int nbits, int* cnt_w,
+                                              int* bad, int (&kept)[kKeep]) {
+  const int lane = threadIdx.x & 63, E = a.num_experts;
   int ci = 0;
   for (int base = beg; base < end; base += 64, ++ci) {
     const int r = base + lane;
@@ -110,33 +99,60 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
     const bool leader = act && ((m >> lane) == 1ull);        // highest lane of its key group
     if (leader) {
       const int c = __popcll(m);
-      if (valid) cnt[w * E + key] += c;
-      else bad_w[w] += c;
+      if (valid) cnt_w[key] += c;
+      else *bad += c;
     }
   }
-  __syncthreads();
+}
 
-  // expert totals, offsets, and per-wave starting slots; tile counts for both tile tables
-  int total_e = 0, bits_e = 0;
-  const bool own = tid < E;                      // E <= 512 < 1024: one expert per thread
-  if (own) {
-    for (int ww = 0; ww < kWaves; ++ww) total_e += cnt[ww * E + tid];
-    bits_e = static_cast<int>((a.packed_bits[tid >> 4] >> (2 * (tid & 15))) & 3u) + 2;
+// Stable placement of one wave's segment: cnt_w[e] holds the wave's next slot for expert e.
+__device__ __forceinline__ void place_segment(const RouteMapArgs& a, int beg, int end, int nbits, int* cnt_w,
+                                              const int (&kept)[kKeep]) {
+  const int lane = threadIdx.x & 63, E = a.num_experts;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int ci = 0;
+  for (int base = beg; base < end; base += 64, ++ci) {
+    const int r = base + lane;
+    const bool act = r < end;
+    int key = E;
+    if (ci < kKeep) {
+#pragma unroll
+      for (int k = 0; k < kKeep; ++k)
+        if (ci == k) key = kept[k];
+    } else {
+      const long long id = act ? load_id(a.ids, a.ids64, r) : -1;
+      key = act && id >= 0 && id < E ? static_cast<int>(id) : E;
+    }
+    const bool valid = act && key < E;
+    const unsigned long long active = __ballot(act);
+    const unsigned long long m = same_key_mask(key, nbits, active);
+    if (valid) {
+      const int pos = cnt_w[key] + __popcll(m & lt);
+      a.sorted_routes[pos] = r;
+      a.slot_expert[pos] = key;
+      a.route_slot[r] = pos;
+    } else if (act) {
+      a.route_slot[r] = -1;
+    }
+    // every lane of the wave has read its running slot above (LDS accesses of one wave complete
+    // in order), so the group leader may now advance it
+    if (valid && ((m >> lane) == 1ull)) cnt_w[key] += __popcll(m);
   }
+}
+
+// Expert totals given, one expert per thread: offsets, tile tables, expert table, scalars. Every
+// thread of the workgroup calls it (it holds workgroup barriers); returns this thread's expert
+// offset (0 for threads past E).
+__device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4* scan_smem) {
+  const int tid = threadIdx.x, E = a.num_experts;
+  const bool own = tid < E;                      // E <= 512 < 1024: one expert per thread
+  const int bits_e = own ? static_cast<int>((a.packed_bits[tid >> 4] >> (2 * (tid & 15))) & 3u) + 2 : 0;
   const int tiles_e = own ? (total_e + a.block_m - 1) / a.block_m : 0;
   const int gtiles_e = own ? (total_e + a.gemm_rows - 1) / a.gemm_rows : 0;
   int4 totals;
-  const int4 offs = block_exclusive_scan4(make_int4(own ? total_e : 0, tiles_e, gtiles_e, own ? bits_e : 0),
-                                          scan_smem, &totals);
+  const int4 offs = block_exclusive_scan4(make_int4(own ? total_e : 0, tiles_e, gtiles_e, bits_e), scan_smem, &totals);
   const int off_e = offs.x, toff_e = offs.y, goff_e = offs.z, boff_e = offs.w;
-  const int n_valid = totals.x, n_tiles = totals.y, n_gtiles = totals.z;
   if (own) {
-    int acc = off_e;
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const int c = cnt[ww * E + tid];
-      cnt[ww * E + tid] = acc;
-      acc += c;
-    }
     a.counts[tid] = total_e;
     a.offsets[tid] = off_e;
     ExpertInfo info;
@@ -159,50 +175,137 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
     }
   }
   if (tid == 0) {
-    a.offsets[E] = n_valid;
-    *a.num_tiles = n_tiles;
-    *a.num_gtiles = n_gtiles;
+    a.offsets[E] = totals.x;
+    *a.num_tiles = totals.y;
+    *a.num_gtiles = totals.z;
     a.splits[0] = a.nsplit[0];
     a.splits[1] = a.nsplit[1];
-    int bad = 0;
-    for (int ww = 0; ww < kWaves; ++ww) bad += bad_w[ww];
     *a.status = bad;
   }
+  return off_e;
+}
+
+// All routes in one workgroup: each wave takes a contiguous segment of R/16 routes.
+__global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
+  __shared__ int cnt[kWaves * kMaxExperts];   // per wave, per expert: count, then running slot
+  __shared__ int4 scan_smem[kWaves];
+  __shared__ int bad_w[kWaves];
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int E = a.num_experts, R = a.routes;
+  for (int i = tid; i < kWaves * E; i += 1024) cnt[i] = 0;
+  if (tid < kWaves) bad_w[tid] = 0;
   __syncthreads();
 
-  // pass 2: stable placement, chunk by chunk in route order within each wave's segment
-  ci = 0;
-  for (int base = beg; base < end; base += 64, ++ci) {
-    const int r = base + lane;
-    const bool act = r < end;
-    int key = E;
-    if (ci < kKeep) {
-#pragma unroll
-      for (int k = 0; k < kKeep; ++k)
-        if (ci == k) key = kept[k];
-    } else {
-      const long long id = act ? load_id(a.ids, a.ids64, r) : -1;
-      key = act && id >= 0 && id < E ? static_cast<int>(id) : E;
+  const int nbits = 32 - __clz(E);              // keys 0..E (E marks an invalid id)
+  const int seg = (R + kWaves - 1) / kWaves;
+  const int beg = w * seg, end = min(R, beg + seg);
+  int kept[kKeep];
+  count_segment(a, beg, end, nbits, cnt + w * E, bad_w + w, kept);
+  __syncthreads();
+
+  int total_e = 0, bad = 0;
+  if (tid < E)
+    for (int ww = 0; ww < kWaves; ++ww) total_e += cnt[ww * E + tid];
+  if (tid == 0)
+    for (int ww = 0; ww < kWaves; ++ww) bad += bad_w[ww];
+  const int off_e = publish_tables(a, total_e, bad, scan_smem);
+  if (tid < E) {                                 // per-wave starting slots
+    int acc = off_e;
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const int c = cnt[ww * E + tid];
+      cnt[ww * E + tid] = acc;
+      acc += c;
     }
-    const bool valid = act && key < E;
-    const unsigned long long active = __ballot(act);
-    const unsigned long long m = same_key_mask(key, nbits, active);
-    if (valid) {
-      const int pos = cnt[w * E + key] + __popcll(m & lt);
-      a.sorted_routes[pos] = r;
-      a.slot_expert[pos] = key;
-      a.route_slot[r] = pos;
-    } else if (act) {
-      a.route_slot[r] = -1;
-    }
-    // every lane of the wave has read its running slot above (LDS accesses of one wave complete
-    // in order), so the group leader may now advance it
-    if (valid && ((m >> lane) == 1ull)) cnt[w * E + key] += __popcll(m);
+  }
+  __syncthreads();
+  place_segment(a, beg, end, nbits, cnt + w * E, kept);
+}
+
+// Large batches, launch 1 of 2: workgroup g counts routes [g * kRouteChunk, (g + 1) * kRouteChunk)
+// per expert into wg_counts[g][0..E) and its invalid ids into wg_counts[g][E].
+__global__ __launch_bounds__(1024) void k_route_count(RouteMapArgs a) {
+  __shared__ int cnt[kWaves * kMaxExperts];
+  __shared__ int bad_w[kWaves];
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int E = a.num_experts, R = a.routes;
+  for (int i = tid; i < kWaves * E; i += 1024) cnt[i] = 0;
+  if (tid < kWaves) bad_w[tid] = 0;
+  __syncthreads();
+  const int nbits = 32 - __clz(E);
+  const int beg = min(R, static_cast<int>(blockIdx.x) * kRouteChunk + w * 64), end = min(R, beg + 64);
+  int kept[kKeep];
+  count_segment(a, beg, end, nbits, cnt + w * E, bad_w + w, kept);
+  __syncthreads();
+  int32_t* out = a.wg_counts + static_cast<size_t>(blockIdx.x) * (E + 1);
+  if (tid < E) {
+    int c = 0;
+    for (int ww = 0; ww < kWaves; ++ww) c += cnt[ww * E + tid];
+    out[tid] = c;
+  }
+  if (tid == 0) {
+    int b = 0;
+    for (int ww = 0; ww < kWaves; ++ww) b += bad_w[ww];
+    out[E] = b;
   }
 }
 
+// Large batches, launch 2 of 2: every workgroup derives the expert offsets from all workgroups'
+// counts, recounts its own chunk per wave and places it; workgroup 0 also writes the tables. The
+// slot of a route is its expert's offset + the routes of that expert in earlier workgroups + in
+// earlier waves of this workgroup + earlier lanes of its chunk: stable token-major order.
+__global__ __launch_bounds__(1024) void k_route_place(RouteMapArgs a) {
+  __shared__ int cnt[kWaves * kMaxExperts];
+  __shared__ int4 scan_smem[kWaves];
+  __shared__ int bad_w[kWaves];
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int E = a.num_experts, R = a.routes;
+  const int G = gridDim.x, g = blockIdx.x;
+  for (int i = tid; i < kWaves * E; i += 1024) cnt[i] = 0;
+  if (tid < kWaves) bad_w[tid] = 0;
+  __syncthreads();
+  const int nbits = 32 - __clz(E);
+  const int beg = min(R, g * kRouteChunk + w * 64), end = min(R, beg + 64);
+  int kept[kKeep];
+  count_segment(a, beg, end, nbits, cnt + w * E, bad_w + w, kept);
+
+  int total_e = 0, before_e = 0, bad = 0;
+  if (tid < E) {
+    for (int gg = 0; gg < G; ++gg) {
+      const int c = a.wg_counts[static_cast<size_t>(gg) * (E + 1) + tid];
+      total_e += c;
+      if (gg < g) before_e += c;
+    }
+  }
+  if (tid == 0)
+    for (int gg = 0; gg < G; ++gg) bad += a.wg_counts[static_cast<size_t>(gg) * (E + 1) + E];
+  __syncthreads();                               // cnt complete
+  int off_e;
+  if (g == 0) {
+    off_e = publish_tables(a, total_e, bad, scan_smem);
+  } else {
+    int4 totals;
+    off_e = block_exclusive_scan4(make_int4(tid < E ? total_e : 0, 0, 0, 0), scan_smem, &totals).x;
+  }
+  if (tid < E) {
+    int acc = off_e + before_e;
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const int c = cnt[ww * E + tid];
+      cnt[ww * E + tid] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+  place_segment(a, beg, end, nbits, cnt + w * E, kept);
+}
+
 void launch_route_map(const RouteMapArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_map, dim3(1), dim3(1024), 0, s, a);
+  if (a.routes <= kRouteSingleMax) {
+    hipLaunchKernelGGL(k_route_map, dim3(1), dim3(1024), 0, s, a);
+    return;
+  }
+  const unsigned groups = static_cast<unsigned>((a.routes + kRouteChunk - 1) / kRouteChunk);
+  hipLaunchKernelGGL(k_route_count, dim3(groups), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(k_route_place, dim3(groups), dim3(1024), 0, s, a);
 }
 
 }  // namespace tmoe

@@ -70,7 +70,7 @@ int tile_rows(int mg) { return mg >= 8 ? 128 : 16 * mg; }
 int fp16_pitch(int k) { return (2 * k) % 512 == 0 ? k + 128 : k; }
 
 struct Layout {
-  size_t einfo, counts, offsets, sorted, slot_e, slot, tile_e, tile_r0, tile_rows, scalars, gtiles;
+  size_t einfo, counts, offsets, sorted, slot_e, slot, tile_e, tile_r0, tile_rows, scalars, gtiles, wgc;
   size_t a1, z, b, v, total;
 };
 
@@ -114,6 +114,7 @@ void build_layout(tmoe_plan_s* p) {
   L.tile_rows = take(4ull * p->max_tiles);
   L.scalars = take(32);                               // num_tiles, status, num_gtiles, splits[2]
   L.gtiles = take(16ull * p->max_gtiles);
+  L.wgc = take(4ull * ((R + kRouteChunk - 1) / kRouteChunk) * (p->E + 1));   // per-workgroup route counts
   L.a1 = take(2ull * R * fp16_pitch(p->H));           // fp16 (padded rows), or E4M3 + E8M0 planes
   const long long zrows = max_split_rows(R, p->H / 32, p->H / 128 > 0 ? p->H / 128 : 1);
   L.z = take(4ull * zrows * 2 * p->I);
@@ -208,6 +209,7 @@ void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_ro
   a.nsplit[0] = sh[0].most;
   a.nsplit[1] = sh[1].most;
   a.slot_expert = at<int32_t>(scratch, p->lay.slot_e);
+  a.wg_counts = at<int32_t>(scratch, p->lay.wgc);
   a.gtiles = at<int4>(scratch, p->lay.gtiles);
   a.einfo = at<ExpertInfo>(scratch, p->lay.einfo);
   std::memcpy(a.packed_bits, p->packed_bits, sizeof(a.packed_bits));

@@ -29,6 +29,7 @@ struct RouteMapArgs {
   int32_t* splits;          // [2] K splits of FC1 and FC2, published for the consumers and tests
   int nsplit[2];            // the host's split counts
   int32_t* slot_expert;     // [R]: expert of each slot
+  int32_t* wg_counts;       // [workgroups][E + 1]: per-workgroup counts (large batches; E = invalid)
   ExpertInfo* einfo;
   uint32_t packed_bits[32]; // 2 bits per expert: bits - 2
 };
@@ -105,6 +106,10 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
   int routes;                // R: row stride between split planes
 };
 
+// one workgroup for up to kRouteSingleMax routes, else a counting and a placement launch over
+// workgroups of kRouteChunk routes each
+constexpr int kRouteChunk = 1024;
+constexpr int kRouteSingleMax = 4096;
 void launch_route_map(const RouteMapArgs& a, hipStream_t s);
 void launch_rotate(const RotateArgs& a, bool mx, hipStream_t s);
 void launch_act(const ActArgs& a, bool mx, hipStream_t s);
