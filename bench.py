@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2516.6
 MFMA_F8_PEAK_TFLOPS = 5033.2
-STAGES = ["route_map", "rotate", "fc1", "act", "fc2", "combine"]
+STAGES = ["route_map", "fc1", "act", "fc2", "combine"]
 COPY_FOOTPRINT = 1.0e9
 # Stored FETCH_SIZE / WRITE_SIZE counters of the headline kernel and the sources they were taken with
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_f16_small_fc1_decode_T16_traffic.txt")
@@ -114,7 +114,7 @@ class Bench:
         return best
 
     def _staged_ms(self, n: int) -> dict:
-        """Per-stage ms over n full forwards, each issued as its six stages with timing events between
+        """Per-stage ms over n full forwards, each issued as its five stages with timing events between
         them on the launch stream. A bounded spin kernel holds the stream while every launch is queued,
         so the GPU then runs them back to back and the events see GPU time, not host launch gaps."""
         torch = self.torch

@@ -140,11 +140,11 @@ tmoe_status tmoe_forward_w4a8(tmoe_plan_t plan, const void *x_bf16, const void *
                               const float *topk_w, int32_t T, const tmoe_weights *weights,
                               float *y, void *scratch, size_t scratch_bytes, void *stream);
 
-/* Run only stages first..last (0 route map, 1 input rotation + quantize, 2 FC1, 3 activation,
- * 4 FC2, 5 output rotation + combine) of tmoe_forward_w4a16 (w4a8 = 0) or tmoe_forward_w4a8
- * (w4a8 = 1), with that call's arguments and checks. A stage reads what the earlier stages of a
- * call with the same T, ids and precision left in scratch, so stages 0..5 issued in order, in one
- * call or several, equal one forward call. Lets a caller put timing events between the launches. */
+/* Run only stages first..last (0 route map with the input rotation + quantize, 1 FC1,
+ * 2 activation, 3 FC2, 4 output rotation + combine) of tmoe_forward_w4a16 (w4a8 = 0) or
+ * tmoe_forward_w4a8 (w4a8 = 1), with that call's arguments and checks. A stage reads what the
+ * earlier stages of a call with the same T, ids and precision left in scratch, so stages 0..4
+ * issued in order, in one call or several, equal one forward call. Lets a caller put timing events between the launches. */
 tmoe_status tmoe_forward_stages(tmoe_plan_t plan, int32_t w4a8, int32_t first, int32_t last,
                                 const void *x_bf16, const void *topk_ids, const float *topk_w,
                                 int32_t T, const tmoe_weights *weights, float *y, void *scratch,
@@ -169,9 +169,10 @@ tmoe_status tmoe_debug_mxfp8(const float *in, int64_t rows, int32_t cols, uint8_
 tmoe_status tmoe_debug_rotate(float *rows_data, int64_t rows, int32_t n, void *stream);
 
 typedef struct {                 /* where a forward call leaves its intermediates, for tests */
-  void *a1;                      /* [T*k][a1_pitch] fp16 (W4A16) or E4M3 bytes (W4A8), slot order;
-                                    the first H entries of each row are the rotated input           */
-  uint8_t *a1_scale;             /* [T*k][H/32] E8M0 (W4A8)                                      */
+  void *a1;                      /* [T*k][a1_pitch] fp16 (W4A16) or E4M3 bytes (W4A8), route order
+                                    (row t*k + j); the first H entries of each row are the rotated
+                                    input                                                          */
+  uint8_t *a1_scale;             /* [T*k][H/32] E8M0 (W4A8), route order                         */
   float *z;                      /* [splits[0]][T*k][2I] fp32 FC1 partial sums, unscaled, slot order */
   void *b;                       /* [T*k][b_pitch] fp16 or E4M3, slot order (first I entries used) */
   uint8_t *b_scale;              /* [T*k][I/32] E8M0 (W4A8)                                      */

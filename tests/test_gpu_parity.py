@@ -239,7 +239,7 @@ def test_sampled_intermediates_prefill():
         tr = O.route_trace(c.inp, t, j)
         p = int(route_slot[r])
         e = int(c.inp.ids[t, j])
-        a = a1[p].double().cpu().numpy()
+        a = a1[int(r)].double().cpu().numpy()
         assert np.max(np.abs(a - tr["a"])) <= 2e-3 * np.max(np.abs(tr["a"]))
         zz = z[:, p].double().sum(0).cpu().numpy() * c.inp.scale1[e].astype(np.float64)
         assert np.max(np.abs(zz - tr["z"])) <= 5e-3 * np.max(np.abs(tr["z"]))

@@ -13,6 +13,7 @@
 // ballots per chunk, independent of how many distinct experts the chunk holds.
 #include "tmoe_device.hpp"
 #include "tmoe_internal.hpp"
+#include "tmoe_rowbody.hpp"
 
 namespace tmoe {
 
@@ -185,8 +186,16 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
   return off_e;
 }
 
-// All routes in one workgroup: each wave takes a contiguous segment of R/16 routes.
-__global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
+// All routes in one workgroup (workgroup 0): each wave takes a contiguous segment of R/16 routes.
+// Workgroups 1.. rotate the input rows, 16 routes each (ROT = false: none).
+template <bool ROT, int EPL, bool MX>
+__global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a, RotateArgs ra) {
+  if constexpr (ROT) {
+    if (blockIdx.x > 0) {
+      rotate_routes<EPL, MX>(ra, (blockIdx.x - 1) * kWaves);
+      return;
+    }
+  }
   __shared__ int cnt[kWaves * kMaxExperts];   // per wave, per expert: count, then running slot
   __shared__ int4 scan_smem[kWaves];
   __shared__ int bad_w[kWaves];
@@ -222,8 +231,16 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a) {
 }
 
 // Large batches, launch 1 of 2: workgroup g counts routes [g * kRouteChunk, (g + 1) * kRouteChunk)
-// per expert into wg_counts[g][0..E) and its invalid ids into wg_counts[g][E].
-__global__ __launch_bounds__(1024) void k_route_count(RouteMapArgs a) {
+// per expert into wg_counts[g][0..E) and its invalid ids into wg_counts[g][E]. Workgroups past the
+// counting ones rotate the input rows, 16 routes each.
+template <bool ROT, int EPL, bool MX>
+__global__ __launch_bounds__(1024) void k_route_count(RouteMapArgs a, RotateArgs ra, int count_groups) {
+  if constexpr (ROT) {
+    if (static_cast<int>(blockIdx.x) >= count_groups) {
+      rotate_routes<EPL, MX>(ra, (blockIdx.x - count_groups) * kWaves);
+      return;
+    }
+  }
   __shared__ int cnt[kWaves * kMaxExperts];
   __shared__ int bad_w[kWaves];
   const int tid = threadIdx.x, w = tid >> 6;
@@ -298,14 +315,30 @@ __global__ __launch_bounds__(1024) void k_route_place(RouteMapArgs a) {
   place_segment(a, beg, end, nbits, cnt + w * E, kept);
 }
 
-void launch_route_map(const RouteMapArgs& a, hipStream_t s) {
-  if (a.routes <= kRouteSingleMax) {
-    hipLaunchKernelGGL(k_route_map, dim3(1), dim3(1024), 0, s, a);
+void launch_route_map(const RouteMapArgs& a, const RotateArgs* ra, bool mx, hipStream_t s) {
+  const unsigned rot_groups = ra ? static_cast<unsigned>((ra->routes + kWaves - 1) / kWaves) : 0;
+  const RotateArgs none{};
+  const RotateArgs& r = ra ? *ra : none;
+  auto go = [&](auto rot, auto epl, auto m) {
+    constexpr bool ROT = decltype(rot)::value;
+    constexpr int E = decltype(epl)::value;
+    constexpr bool M = decltype(m)::value;
+    if (a.routes <= kRouteSingleMax) {
+      hipLaunchKernelGGL((k_route_map<ROT, E, M>), dim3(1 + rot_groups), dim3(1024), 0, s, a, r);
+      return;
+    }
+    const int groups = (a.routes + kRouteChunk - 1) / kRouteChunk;
+    hipLaunchKernelGGL((k_route_count<ROT, E, M>), dim3(groups + rot_groups), dim3(1024), 0, s, a, r, groups);
+    hipLaunchKernelGGL(k_route_place, dim3(groups), dim3(1024), 0, s, a);
+  };
+  if (!ra) {
+    go(std::false_type{}, std::integral_constant<int, 1>{}, std::false_type{});
     return;
   }
-  const unsigned groups = static_cast<unsigned>((a.routes + kRouteChunk - 1) / kRouteChunk);
-  hipLaunchKernelGGL(k_route_count, dim3(groups), dim3(1024), 0, s, a);
-  hipLaunchKernelGGL(k_route_place, dim3(groups), dim3(1024), 0, s, a);
+  dispatch_epl(ra->rot, [&](auto epl) {
+    if (mx) go(std::true_type{}, epl, std::true_type{});
+    else go(std::true_type{}, epl, std::false_type{});
+  });
 }
 
 }  // namespace tmoe

@@ -1,8 +1,6 @@
 // k_rowops.hip -- per-row kernels around the two trellis GEMMs, one wavefront per row.
 //
-//  k_rotate : a = R_H(su1_e * x_t) for every route slot, stored as fp16 or MXFP8 (E4M3 values
-//             with one E8M0 scale per 32). One fused launch for rotation and quantization, as in
-//             "serve canonical Fruit QSRT atoms", Hot path.
+//  (the input rotation runs in the route-map launch, k_route_map.hip)
 //  k_act    : the activation epilogue between FC1 and FC2 in the pages' order
 //             R_I -> svh -> silu(gate) * up -> suh_down -> R_I ("integrate EXL3 Trellis into the
 //             fused W4A16 API", review of kernel.py), with the FC1 channel scales applied first.
@@ -15,14 +13,11 @@
 // order, with all loads of a row issued before the first add so one memory latency covers them.
 #include "tmoe_device.hpp"
 #include "tmoe_internal.hpp"
+#include "tmoe_rowbody.hpp"
 
 namespace tmoe {
 
 namespace {
-
-__device__ __forceinline__ long long route_expert(const void* ids, int ids64, int r) {
-  return ids64 ? static_cast<const long long*>(ids)[r] : static_cast<long long>(static_cast<const int*>(ids)[r]);
-}
 
 // out[i] = sum over s < splits, ascending, of src[s * plane + 64 * i] for i < S, with splits <= SMAX
 // (the kernels here pass splits = SMAX, the host's split count). Planes are loaded SU at a time;
@@ -56,64 +51,6 @@ __device__ __forceinline__ void sum_splits(const float* __restrict__ src, size_t
 template <int S, int SMAX>
 constexpr int splits_unroll(int rows) {   // planes loaded per round: about 64 loads in flight per lane
   return SMAX * S * rows <= 64 ? SMAX : (64 / (S * rows) >= 1 ? 64 / (S * rows) : 1);
-}
-
-// Visit the rotation blocks of a row: one power-of-two segment of EPL values per lane, or (EPL = 0)
-// 128-point blocks (2 per lane) followed by an optional 64-point block (1 per lane).
-template <int EPL, class Body>
-__device__ __forceinline__ void for_segments(const RowRot& rot, Body& body) {
-  if constexpr (EPL > 0) {
-    body.template run<EPL>(0);
-  } else {
-    for (int b = 0; b < rot.nblk128; ++b) body.template run<2>(b * 128);
-    if (rot.tail64) body.template run<1>(rot.nblk128 * 128);
-  }
-}
-
-// MXFP8 of one value per lane; each 32-lane half of the wavefront is one 32-value block.
-__device__ __forceinline__ void mx_store(float v, int lane, uint8_t* q_row, uint8_t* s_row, int idx) {
-  const float amax = half_wave_amax(v);
-  const int e = mx_exponent(amax);
-  float sv = ldexpf(v, -e);
-  sv = fminf(fmaxf(sv, -448.0f), 448.0f);     // saturating E4M3 (only a subnormal quotient can exceed)
-  q_row[idx] = static_cast<uint8_t>(fp8x2_from_f32(sv, 0.0f) & 0xffu);
-  if ((lane & 31) == 0) s_row[idx >> 5] = static_cast<uint8_t>(e + 127);
-}
-
-template <bool MX>
-struct RotateBody {
-  const RotateArgs& a;
-  int lane, p, t, e, H;
-  template <int S>
-  __device__ __forceinline__ void run(int off) {
-    float v[S];
-    const uint16_t* xr = a.x + static_cast<size_t>(t) * H + off + lane;
-    const uint16_t* sr = a.su1 + static_cast<size_t>(e) * H + off + lane;
-#pragma unroll
-    for (int i = 0; i < S; ++i) v[i] = bf16_to_f32(xr[64 * i]) * h2f(sr[64 * i]);
-    if (!a.rot.identity) fwht_segment<S>(v, lane);
-    if constexpr (!MX) {
-      _Float16* out = static_cast<_Float16*>(a.a1) + static_cast<size_t>(p) * a.lda + off + lane;
-#pragma unroll
-      for (int i = 0; i < S; ++i) out[64 * i] = static_cast<_Float16>(v[i]);
-    } else {
-      uint8_t* q = static_cast<uint8_t*>(a.a1) + static_cast<size_t>(p) * H;
-      uint8_t* sc = a.a1_scale + static_cast<size_t>(p) * (H / 32);
-#pragma unroll
-      for (int i = 0; i < S; ++i) mx_store(v[i], lane, q, sc, off + 64 * i + lane);
-    }
-  }
-};
-
-template <int EPL, bool MX>
-__global__ __launch_bounds__(256) void k_rotate(RotateArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (p >= a.routes || p >= a.offsets[a.num_experts]) return;   // whole wavefront leaves together
-  const int t = a.sorted_routes[p] / a.top_k;
-  const int e = a.slot_expert[p];
-  RotateBody<MX> body{a, lane, p, t, e, a.rot.n};
-  for_segments<EPL>(a.rot, body);
 }
 
 template <bool MX, int SMAX>
@@ -303,20 +240,6 @@ __global__ __launch_bounds__(256) void k_debug_mxfp8(const float* in, long long 
   }
 }
 
-template <class F>
-void dispatch_epl(const RowRot& rot, F&& f) {
-  if (!rot.pow2) { f(std::integral_constant<int, 0>{}); return; }
-  switch (rot.n / 64) {
-    case 1: f(std::integral_constant<int, 1>{}); break;
-    case 2: f(std::integral_constant<int, 2>{}); break;
-    case 4: f(std::integral_constant<int, 4>{}); break;
-    case 8: f(std::integral_constant<int, 8>{}); break;
-    case 16: f(std::integral_constant<int, 16>{}); break;
-    case 32: f(std::integral_constant<int, 32>{}); break;
-    default: f(std::integral_constant<int, 64>{}); break;
-  }
-}
-
 inline unsigned blocks_for(long long rows) { return static_cast<unsigned>((rows + 3) / 4); }
 
 template <class F>
@@ -342,14 +265,6 @@ int combine_waves(int hidden, int top_k) {
 }
 
 }  // namespace
-
-void launch_rotate(const RotateArgs& a, bool mx, hipStream_t s) {
-  dispatch_epl(a.rot, [&](auto epl) {
-    constexpr int E = decltype(epl)::value;
-    if (mx) hipLaunchKernelGGL((k_rotate<E, true>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_rotate<E, false>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
-  });
-}
 
 void launch_act(const ActArgs& a, bool mx, hipStream_t s) {
   dispatch_epl(a.rot, [&](auto epl) {

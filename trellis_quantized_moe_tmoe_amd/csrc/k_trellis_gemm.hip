@@ -54,6 +54,12 @@ __device__ __forceinline__ gptr<T> uniform_ptr(const T* p) {
 template <int MG>
 constexpr int ring_words() { return DF * (2 * NS * 32 + MG * 256); }
 
+// Operand row of slot p: the FC1 input is stored per route (arow maps slot -> route), the FC2 input
+// per slot.
+__device__ __forceinline__ long long operand_row(const GemmArgs& a, int p) {
+  return a.arow ? static_cast<long long>(a.arow[p]) : static_cast<long long>(p);
+}
+
 template <int BITS, int MG>
 __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng, int s, int splits, int lane,
                                          uint32_t* ring, uint32_t mask, uint32_t orv) {
@@ -71,7 +77,7 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
   const int nt0 = ng * NS;
   const gptr<uint32_t> mat = uniform_ptr(reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS) +
                                          static_cast<size_t>(nt0) * TW);
-  const gptr<_Float16> A = uniform_ptr(static_cast<const _Float16*>(a.a) + static_cast<size_t>(row0) * a.lda);
+  const gptr<_Float16> A = uniform_ptr(static_cast<const _Float16*>(a.a));
   // staging of trellis words: lane L < BW/4 copies 16-byte chunk L, [tile row][strip][chunk] order
   const bool stager = lane < BW / 4;
   const int st_tile = lane / (NS * CPT), st_strip = (lane / CPT) % NS, st_chunk = lane % CPT;
@@ -81,9 +87,9 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
   const int j0 = window_word<BITS>(q);
   const int rd_a = (grp >> 1) * NS * TW + (j0 < 0 ? j0 + TW : j0);
   const int rd_b = (grp >> 1) * NS * TW + ((j0 + 1 == TW) ? 0 : j0 + 1);
-  int aoff[MG];
+  long long aoff[MG];
 #pragma unroll
-  for (int mg = 0; mg < MG; ++mg) aoff[mg] = min(16 * mg + col, rows - 1) * a.lda + 8 * grp;
+  for (int mg = 0; mg < MG; ++mg) aoff[mg] = operand_row(a, row0 + min(16 * mg + col, rows - 1)) * a.lda + 8 * grp;
   // Lanes of the first row group whose row lies beyond the tile load nothing (lane 0's row always
   // exists, so every step still issues the same number of load instructions and the ring's wait
   // counts hold); their LDS bytes are stale and only feed output rows that are never stored. The
@@ -235,11 +241,11 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
   const int nt0 = (nb * 4 + wv) * SPW;                    // this wavefront's first strip
   const gptr<uint32_t> mat = uniform_ptr(reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS) +
                                          static_cast<size_t>(nt0) * TW);
-  const gptr<_Float16> A = uniform_ptr(static_cast<const _Float16*>(a.a) + static_cast<size_t>(row0) * a.lda);
+  const gptr<_Float16> A = uniform_ptr(static_cast<const _Float16*>(a.a));
   // A rows copied by this wavefront: row groups 2 * wv and 2 * wv + 1, in MFMA operand order
-  int aoff[2];
+  long long aoff[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) aoff[i] = min(16 * (2 * wv + i) + col, rows - 1) * a.lda + 8 * grp;
+  for (int i = 0; i < 2; ++i) aoff[i] = operand_row(a, row0 + min(16 * (2 * wv + i) + col, rows - 1)) * a.lda + 8 * grp;
   // trellis words: per step two tile rows x SPW adjacent tiles = two runs of RUN words; lane
   // L < RUN / 2 copies 16-byte piece L % (RUN / 4) of run L / (RUN / 4)
   const bool stager = lane < RUN / 2;
@@ -410,7 +416,7 @@ __device__ __forceinline__ void unit_f8(const GemmArgs& a, const int4 t, int ng,
   for (int mg = 0; mg < MG; ++mg) {
     const int r = 16 * mg + col;
     aok[mg] = r < rows;
-    const size_t rr = static_cast<size_t>(row0 + (aok[mg] ? r : 0));
+    const size_t rr = static_cast<size_t>(operand_row(a, row0 + (aok[mg] ? r : 0)));
     arow[mg] = A + rr * a.K + 16 * grp;
     srow[mg] = a.a_scale + rr * kblocks + grp;
   }

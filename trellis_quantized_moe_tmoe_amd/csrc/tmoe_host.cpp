@@ -184,8 +184,9 @@ int big_cols(const tmoe_plan_s* p, bool fp8) {
   return 0;
 }
 
+// With `rot` set, the same launch also writes the rotated input operand of every route.
 void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_rows, const GemmShape (&sh)[2],
-                       void* scratch, hipStream_t st) {
+                       void* scratch, const RotateArgs* rot, bool fp8, hipStream_t st) {
   RouteMapArgs a;
   std::memset(&a, 0, sizeof(a));
   a.ids = ids;
@@ -213,7 +214,7 @@ void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_ro
   a.gtiles = at<int4>(scratch, p->lay.gtiles);
   a.einfo = at<ExpertInfo>(scratch, p->lay.einfo);
   std::memcpy(a.packed_bits, p->packed_bits, sizeof(a.packed_bits));
-  launch_route_map(a, st);
+  launch_route_map(a, rot, fp8, st);
 }
 
 tmoe_status check_common(const tmoe_plan_s* p, const void* ids, int T, void* scratch, size_t bytes) {
@@ -226,10 +227,10 @@ tmoe_status check_common(const tmoe_plan_s* p, const void* ids, int T, void* scr
   return check_scratch(p, scratch, bytes);
 }
 
-// Stages: 0 route map, 1 input rotation, 2 FC1, 3 activation, 4 FC2, 5 combine.
+// Stages: 0 route map with the input rotation, 1 FC1, 2 activation, 3 FC2, 4 combine.
 tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* w, int32_t T,
                     const tmoe_weights* wt, float* y, void* scratch, size_t bytes, void* stream, bool fp8,
-                    int first = 0, int last = 5) {
+                    int first = 0, int last = 4) {
   tmoe_status st = check_common(p, ids, T, scratch, bytes);
   if (st != TMOE_OK) return st;
   if (fp8 && !p->fp8_ok) return TMOE_ERR_UNSUPPORTED;
@@ -248,10 +249,6 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   const int gemm_rows = tile_rows(mg);
   const GemmShape sh[2] = {gemm_shape(p, R, mg, fp8, 1), gemm_shape(p, R, mg, fp8, 2)};
 
-  (void)hipGetLastError();   // clear a stale error so the check below reports this call only
-  auto on = [&](int stage) { return first <= stage && stage <= last; };
-  if (on(0)) enqueue_route_map(p, ids, T, gemm_rows, sh, scratch, s);
-
   const int32_t* sorted = at<int32_t>(scratch, p->lay.sorted);
   const int32_t* slot_expert = at<int32_t>(scratch, p->lay.slot_e);
   const int32_t* offsets = at<int32_t>(scratch, p->lay.offsets);
@@ -264,10 +261,9 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
 
   RotateArgs ra;
   ra.x = static_cast<const uint16_t*>(x);
+  ra.ids = ids;
+  ra.ids64 = p->ids64;
   ra.top_k = p->K;
-  ra.sorted_routes = sorted;
-  ra.slot_expert = slot_expert;
-  ra.offsets = offsets;
   ra.num_experts = p->E;
   ra.su1 = wt->su1;
   ra.rot = make_rot(p->H, p->rotation == TMOE_ROT_IDENTITY);
@@ -275,7 +271,10 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   ra.a1_scale = a1s;
   ra.lda = fp16_pitch(p->H);
   ra.routes = static_cast<int>(R);
-  if (on(1)) launch_rotate(ra, fp8, s);
+
+  (void)hipGetLastError();   // clear a stale error so the check below reports this call only
+  auto on = [&](int stage) { return first <= stage && stage <= last; };
+  if (on(0)) enqueue_route_map(p, ids, T, gemm_rows, sh, scratch, &ra, fp8, s);
 
   GemmArgs g1;
   g1.payload = wt->payload;
@@ -291,8 +290,9 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g1.lda = fp16_pitch(p->H);
   g1.nsplit = sh[0].most;
   g1.routes = static_cast<int>(R);
+  g1.arow = sorted;
   const int waves1 = sh[0].waves;
-  if (on(2)) {
+  if (on(1)) {
     if (fp8) launch_gemm_f8(g1, 1, p->uniform_bits, mg, waves1, s);
     else launch_gemm_f16(g1, 1, p->uniform_bits, mg, waves1, s);
   }
@@ -311,7 +311,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   aa.b_scale = bs;
   aa.ldb = fp16_pitch(p->I);
   aa.routes = static_cast<int>(R);
-  if (on(3)) launch_act(aa, fp8, s);
+  if (on(2)) launch_act(aa, fp8, s);
 
   GemmArgs g2 = g1;
   g2.fc2_words_per_bit = 2LL * p->H * p->I / 16;
@@ -322,8 +322,9 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g2.N = p->H;
   g2.lda = fp16_pitch(p->I);
   g2.nsplit = sh[1].most;
+  g2.arow = nullptr;
   const int waves2 = sh[1].waves;
-  if (on(4)) {
+  if (on(3)) {
     if (fp8) launch_gemm_f8(g2, 2, p->uniform_bits, mg, waves2, s);
     else launch_gemm_f16(g2, 2, p->uniform_bits, mg, waves2, s);
   }
@@ -342,7 +343,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   ca.sv2 = wt->sv2;
   ca.rot = make_rot(p->H, p->rotation == TMOE_ROT_IDENTITY);
   ca.y = y;
-  if (on(5)) launch_combine(ca, s);
+  if (on(4)) launch_combine(ca, s);
 
   return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
 }
@@ -435,7 +436,7 @@ tmoe_status tmoe_build_route_map(tmoe_plan_t p, const void* ids, int32_t T, void
   const int gemm_rows = tile_rows(mg);
   const GemmShape sh[2] = {gemm_shape(p, R, mg, false, 1), gemm_shape(p, R, mg, false, 2)};
   (void)hipGetLastError();
-  enqueue_route_map(p, ids, T, gemm_rows, sh, scratch, static_cast<hipStream_t>(stream));
+  enqueue_route_map(p, ids, T, gemm_rows, sh, scratch, nullptr, false, static_cast<hipStream_t>(stream));
   *view = make_view(p, scratch);
   return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
 }
@@ -453,7 +454,7 @@ tmoe_status tmoe_forward_w4a8(tmoe_plan_t p, const void* x, const void* ids, con
 tmoe_status tmoe_forward_stages(tmoe_plan_t p, int32_t w4a8, int32_t first, int32_t last, const void* x,
                                 const void* ids, const float* w, int32_t T, const tmoe_weights* wt, float* y,
                                 void* scratch, size_t bytes, void* stream) {
-  if ((w4a8 != 0 && w4a8 != 1) || first < 0 || last > 5 || first > last) return TMOE_ERR_INVALID_ARG;
+  if ((w4a8 != 0 && w4a8 != 1) || first < 0 || last > 4 || first > last) return TMOE_ERR_INVALID_ARG;
   return forward(p, x, ids, w, T, wt, y, scratch, bytes, stream, w4a8 != 0, first, last);
 }
 

@@ -44,12 +44,11 @@ struct RowRot {
   int identity;
 };
 
-struct RotateArgs {          // a = R_H(su1_e * x_t) per slot, fp16 or MXFP8
+struct RotateArgs {          // a = R_H(su1_e * x_t) per route, fp16 or MXFP8, row = route index
   const uint16_t* x;         // bf16 [T][H]
+  const void* ids;           // [T][k] expert ids (routes with an invalid id are skipped)
+  int ids64;
   int top_k;
-  const int32_t* sorted_routes;
-  const int32_t* slot_expert;
-  const int32_t* offsets;    // offsets[E] = valid slots
   int num_experts;
   const uint16_t* su1;       // [E][H]
   RowRot rot;
@@ -95,7 +94,8 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
   const uint16_t* payload;
   const ExpertInfo* einfo;
   long long fc2_words_per_bit;  // FC2 region starts after H*2I*bits/16 words: pass H*2I/16 or 0
-  const void* a;             // fp16 [R][lda] or e4m3 [R][K]
+  const void* a;             // fp16 [rows][lda] or e4m3 [rows][K]
+  const int32_t* arow;       // operand row of each slot (FC1: the slot's route), or null: row = slot
   const uint8_t* a_scale;    // [R][K/32] (fp8 only)
   float* out;                // [splits][R][N]
   const int4* gtiles;
@@ -110,8 +110,8 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
 // workgroups of kRouteChunk routes each
 constexpr int kRouteChunk = 1024;
 constexpr int kRouteSingleMax = 4096;
-void launch_route_map(const RouteMapArgs& a, hipStream_t s);
-void launch_rotate(const RotateArgs& a, bool mx, hipStream_t s);
+// the route map and, in the same launch (extra workgroups, independent work), the input rotation
+void launch_route_map(const RouteMapArgs& a, const RotateArgs* rot, bool mx, hipStream_t s);
 void launch_act(const ActArgs& a, bool mx, hipStream_t s);
 void launch_combine(const CombineArgs& a, hipStream_t s);
 // fc: 1 or 2 (names the kernel); bits: the width shared by every expert (2, 3, 4) or 0 if mixed;

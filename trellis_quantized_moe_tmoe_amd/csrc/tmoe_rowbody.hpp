@@ -1,0 +1,89 @@
+// tmoe_rowbody.hpp -- row helpers shared by the route-map launch (input rotation) and the
+// activation / combine kernels: rotation-block traversal, MXFP8 stores, the input rotation body.
+#pragma once
+#include "tmoe_device.hpp"
+#include "tmoe_internal.hpp"
+
+namespace tmoe {
+
+__device__ __forceinline__ long long route_expert(const void* ids, int ids64, int r) {
+  return ids64 ? static_cast<const long long*>(ids)[r] : static_cast<long long>(static_cast<const int*>(ids)[r]);
+}
+
+// Visit the rotation blocks of a row: one power-of-two segment of EPL values per lane, or (EPL = 0)
+// 128-point blocks (2 per lane) followed by an optional 64-point block (1 per lane).
+template <int EPL, class Body>
+__device__ __forceinline__ void for_segments(const RowRot& rot, Body& body) {
+  if constexpr (EPL > 0) {
+    body.template run<EPL>(0);
+  } else {
+    for (int b = 0; b < rot.nblk128; ++b) body.template run<2>(b * 128);
+    if (rot.tail64) body.template run<1>(rot.nblk128 * 128);
+  }
+}
+
+// MXFP8 of one value per lane; each 32-lane half of the wavefront is one 32-value block.
+__device__ __forceinline__ void mx_store(float v, int lane, uint8_t* q_row, uint8_t* s_row, int idx) {
+  const float amax = half_wave_amax(v);
+  const int e = mx_exponent(amax);
+  float sv = ldexpf(v, -e);
+  sv = fminf(fmaxf(sv, -448.0f), 448.0f);     // saturating E4M3 (only a subnormal quotient can exceed)
+  q_row[idx] = static_cast<uint8_t>(fp8x2_from_f32(sv, 0.0f) & 0xffu);
+  if ((lane & 31) == 0) s_row[idx >> 5] = static_cast<uint8_t>(e + 127);
+}
+
+// Input rotation of one route (token t, expert e): a = R_H(su1_e * x_t) into operand row p.
+template <bool MX>
+struct RotateBody {
+  const RotateArgs& a;
+  int lane, p, t, e, H;     // p: operand row (the route index)
+  template <int S>
+  __device__ __forceinline__ void run(int off) {
+    float v[S];
+    const uint16_t* xr = a.x + static_cast<size_t>(t) * H + off + lane;
+    const uint16_t* sr = a.su1 + static_cast<size_t>(e) * H + off + lane;
+#pragma unroll
+    for (int i = 0; i < S; ++i) v[i] = bf16_to_f32(xr[64 * i]) * h2f(sr[64 * i]);
+    if (!a.rot.identity) fwht_segment<S>(v, lane);
+    if constexpr (!MX) {
+      _Float16* out = static_cast<_Float16*>(a.a1) + static_cast<size_t>(p) * a.lda + off + lane;
+#pragma unroll
+      for (int i = 0; i < S; ++i) out[64 * i] = static_cast<_Float16>(v[i]);
+    } else {
+      uint8_t* q = static_cast<uint8_t*>(a.a1) + static_cast<size_t>(p) * H;
+      uint8_t* sc = a.a1_scale + static_cast<size_t>(p) * (H / 32);
+#pragma unroll
+      for (int i = 0; i < S; ++i) mx_store(v[i], lane, q, sc, off + 64 * i + lane);
+    }
+  }
+};
+
+// Host: call f with the rotation's values per lane as a compile-time constant (0 = 128/64 blocks).
+template <class F>
+void dispatch_epl(const RowRot& rot, F&& f) {
+  if (!rot.pow2) { f(std::integral_constant<int, 0>{}); return; }
+  switch (rot.n / 64) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 8: f(std::integral_constant<int, 8>{}); break;
+    case 16: f(std::integral_constant<int, 16>{}); break;
+    case 32: f(std::integral_constant<int, 32>{}); break;
+    default: f(std::integral_constant<int, 64>{}); break;
+  }
+}
+
+// Workgroup-level input rotation, one route per wavefront: route r = first + wave. Used by the
+// route-map launch for its extra workgroups (the rotation does not depend on the route map).
+template <int EPL, bool MX>
+__device__ __forceinline__ void rotate_routes(const RotateArgs& a, int first) {
+  const int lane = threadIdx.x & 63;
+  const int r = first + static_cast<int>(threadIdx.x >> 6);
+  if (r >= a.routes) return;
+  const long long e = route_expert(a.ids, a.ids64, r);
+  if (e < 0 || e >= a.num_experts) return;         // dropped route: its row is never read
+  RotateBody<MX> body{a, lane, r, r / a.top_k, static_cast<int>(e), a.rot.n};
+  for_segments<EPL>(a.rot, body);
+}
+
+}  // namespace tmoe
