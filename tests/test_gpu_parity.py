@@ -149,6 +149,21 @@ def test_layer_w4a16_workgroup_tiles_with_k_splits(T):
     assert err <= TOL_W4A16
 
 
+@pytest.mark.parametrize("name,T,over", [
+    ("tiny", 128, dict(experts=2, top_k=1)),   # 128-row tiles, 4 K splits: FC2 runs 1 step per split (odd)
+    ("tiny", 700, dict(experts=2, top_k=1)),   # ~350 rows per expert: two full tiles and a partial one
+    ("tiny", 450, dict(experts=4, top_k=2)),   # ~225 rows per expert
+    ("tiny", 600, dict()),                     # 8 experts of ~150 rows
+    ("wide", 300, dict(hidden=256, inter=128, experts=4, top_k=2)),   # mixed 2/3/4-bit experts
+])
+def test_layer_w4a16_workgroup_tile_edges(name, T, over):
+    c = Case(name, T, **over)
+    y = c.run().cpu().numpy()
+    err = rel_err(y, c.oracle_w4a16)
+    say(f"[result] {c.label} W4A16 rel err {err:.3e}")
+    assert err <= TOL_W4A16
+
+
 def test_w4a16_path_on_w4a8_geometry():
     c = Case("w4a8", 32)
     err = rel_err(c.run().cpu().numpy(), c.oracle_w4a16)

@@ -141,10 +141,28 @@ __device__ __forceinline__ void place_segment(const RouteMapArgs& a, int beg, in
   }
 }
 
+// Per-expert prefix sums kept in LDS while the tile tables are written: slots, block_m tiles, GEMM
+// tiles and payload bit offsets, each with its total in entry E.
+struct TableSmem {
+  int off[kMaxExperts + 1], toff[kMaxExperts + 1], goff[kMaxExperts + 1], boff[kMaxExperts + 1];
+};
+
+// The expert whose range [tab[e], tab[e + 1]) holds i, for 0 <= i < tab[E]: the last e with
+// tab[e] <= i (empty experts before it share its start and come earlier).
+__device__ __forceinline__ int owner_of(const int* tab, int E, int i) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tab[mid] <= i) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // Expert totals given, one expert per thread: offsets, tile tables, expert table, scalars. Every
 // thread of the workgroup calls it (it holds workgroup barriers); returns this thread's expert
-// offset (0 for threads past E).
-__device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4* scan_smem) {
+// offset (0 for threads past E). The tile tables are written by all threads, one tile each in turn.
+__device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4* scan_smem, TableSmem& tb) {
   const int tid = threadIdx.x, E = a.num_experts;
   const bool own = tid < E;                      // E <= 512 < 1024: one expert per thread
   const int bits_e = own ? static_cast<int>((a.packed_bits[tid >> 4] >> (2 * (tid & 15))) & 3u) + 2 : 0;
@@ -152,36 +170,52 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
   const int gtiles_e = own ? (total_e + a.gemm_rows - 1) / a.gemm_rows : 0;
   int4 totals;
   const int4 offs = block_exclusive_scan4(make_int4(own ? total_e : 0, tiles_e, gtiles_e, bits_e), scan_smem, &totals);
-  const int off_e = offs.x, toff_e = offs.y, goff_e = offs.z, boff_e = offs.w;
+  const int off_e = offs.x;
   if (own) {
     a.counts[tid] = total_e;
     a.offsets[tid] = off_e;
     ExpertInfo info;
-    info.word_offset = static_cast<long long>(boff_e) * a.words_per_bit;
+    info.word_offset = static_cast<long long>(offs.w) * a.words_per_bit;
     info.bits = bits_e;
     info.pad = 0;
     a.einfo[tid] = info;
-    for (int t = 0; t < tiles_e; ++t) {
-      a.tile_expert[toff_e + t] = tid;
-      a.tile_row0[toff_e + t] = off_e + t * a.block_m;
-      a.tile_rows[toff_e + t] = min(a.block_m, total_e - t * a.block_m);
-    }
-    for (int t = 0; t < gtiles_e; ++t) {
-      int4 g;
-      g.x = tid | (bits_e << 24);
-      g.y = off_e + t * a.gemm_rows;
-      g.z = min(a.gemm_rows, total_e - t * a.gemm_rows);
-      g.w = static_cast<int>(info.word_offset >> 8);   // expert regions start on 256-word multiples
-      a.gtiles[goff_e + t] = g;
-    }
+    tb.off[tid] = off_e;
+    tb.toff[tid] = offs.y;
+    tb.goff[tid] = offs.z;
+    tb.boff[tid] = offs.w;
   }
   if (tid == 0) {
+    tb.off[E] = totals.x;
+    tb.toff[E] = totals.y;
+    tb.goff[E] = totals.z;
+    tb.boff[E] = totals.w;
     a.offsets[E] = totals.x;
     *a.num_tiles = totals.y;
     *a.num_gtiles = totals.z;
     a.splits[0] = a.nsplit[0];
     a.splits[1] = a.nsplit[1];
     *a.status = bad;
+  }
+  __syncthreads();
+  for (int i = tid; i < totals.y; i += blockDim.x) {
+    const int e = owner_of(tb.toff, E, i);
+    const int t = i - tb.toff[e];
+    const int cnt_e = tb.off[e + 1] - tb.off[e];
+    a.tile_expert[i] = e;
+    a.tile_row0[i] = tb.off[e] + t * a.block_m;
+    a.tile_rows[i] = min(a.block_m, cnt_e - t * a.block_m);
+  }
+  for (int i = tid; i < totals.z; i += blockDim.x) {
+    const int e = owner_of(tb.goff, E, i);
+    const int t = i - tb.goff[e];
+    const int cnt_e = tb.off[e + 1] - tb.off[e];
+    const int b = tb.boff[e + 1] - tb.boff[e];
+    int4 g;
+    g.x = e | (b << 24);
+    g.y = tb.off[e] + t * a.gemm_rows;
+    g.z = min(a.gemm_rows, cnt_e - t * a.gemm_rows);
+    g.w = static_cast<int>((static_cast<long long>(tb.boff[e]) * a.words_per_bit) >> 8);   // expert regions start on 256-word multiples
+    a.gtiles[i] = g;
   }
   return off_e;
 }
@@ -199,6 +233,7 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a, RotateArgs r
   __shared__ int cnt[kWaves * kMaxExperts];   // per wave, per expert: count, then running slot
   __shared__ int4 scan_smem[kWaves];
   __shared__ int bad_w[kWaves];
+  __shared__ TableSmem tb;
   const int tid = threadIdx.x, w = tid >> 6;
   const int E = a.num_experts, R = a.routes;
   for (int i = tid; i < kWaves * E; i += 1024) cnt[i] = 0;
@@ -217,7 +252,7 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a, RotateArgs r
     for (int ww = 0; ww < kWaves; ++ww) total_e += cnt[ww * E + tid];
   if (tid == 0)
     for (int ww = 0; ww < kWaves; ++ww) bad += bad_w[ww];
-  const int off_e = publish_tables(a, total_e, bad, scan_smem);
+  const int off_e = publish_tables(a, total_e, bad, scan_smem, tb);
   if (tid < E) {                                 // per-wave starting slots
     int acc = off_e;
     for (int ww = 0; ww < kWaves; ++ww) {
@@ -274,6 +309,8 @@ __global__ __launch_bounds__(1024) void k_route_place(RouteMapArgs a) {
   __shared__ int cnt[kWaves * kMaxExperts];
   __shared__ int4 scan_smem[kWaves];
   __shared__ int bad_w[kWaves];
+  __shared__ TableSmem tb;
+  __shared__ int bad_all;
   const int tid = threadIdx.x, w = tid >> 6;
   const int E = a.num_experts, R = a.routes;
   const int G = gridDim.x, g = blockIdx.x;
@@ -285,20 +322,38 @@ __global__ __launch_bounds__(1024) void k_route_place(RouteMapArgs a) {
   int kept[kKeep];
   count_segment(a, beg, end, nbits, cnt + w * E, bad_w + w, kept);
 
+  // column tid (an expert, or E: the invalid ids) of all workgroups' counts, eight loads in flight
   int total_e = 0, before_e = 0, bad = 0;
-  if (tid < E) {
-    for (int gg = 0; gg < G; ++gg) {
-      const int c = a.wg_counts[static_cast<size_t>(gg) * (E + 1) + tid];
+  if (tid <= E) {
+    const int32_t* col = a.wg_counts + tid;
+    const size_t pitch = static_cast<size_t>(E + 1);
+    int gg = 0;
+    for (; gg + 8 <= G; gg += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = col[(gg + u) * pitch];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        total_e += c[u];
+        before_e += gg + u < g ? c[u] : 0;
+      }
+    }
+    for (; gg < G; ++gg) {
+      const int c = col[gg * pitch];
       total_e += c;
-      if (gg < g) before_e += c;
+      before_e += gg < g ? c : 0;
+    }
+    if (tid == E) {
+      bad = total_e;
+      total_e = 0;
+      before_e = 0;
     }
   }
-  if (tid == 0)
-    for (int gg = 0; gg < G; ++gg) bad += a.wg_counts[static_cast<size_t>(gg) * (E + 1) + E];
+  if (tid == E) bad_all = bad;
   __syncthreads();                               // cnt complete
   int off_e;
   if (g == 0) {
-    off_e = publish_tables(a, total_e, bad, scan_smem);
+    off_e = publish_tables(a, total_e, bad_all, scan_smem, tb);
   } else {
     int4 totals;
     off_e = block_exclusive_scan4(make_int4(tid < E ? total_e : 0, 0, 0, 0), scan_smem, &totals).x;

@@ -103,8 +103,10 @@ template <int EPL, bool MX, int SMAX>
 __global__ __launch_bounds__(256) void k_act(ActArgs a) {
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (p >= a.routes || p >= a.offsets[a.num_experts]) return;
-  const int e = a.slot_expert[p];
+  if (p >= a.routes) return;
+  const int filled = a.offsets[a.num_experts];   // both loads in flight together
+  const int e = a.slot_expert[p];                // (stale past the filled slots, unused there)
+  if (p >= filled) return;
   ActBody<MX, SMAX> body{a, lane, p, e, a.rot.n, SMAX};
   for_segments<EPL>(a.rot, body);
 }

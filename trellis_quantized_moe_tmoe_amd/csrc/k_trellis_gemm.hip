@@ -330,15 +330,18 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();                                          // the next unit refills the ring
 
+  // the lane's row offset passes through an empty asm so the store offsets are not hoisted out of
+  // the unit loop into VGPRs
   float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
+  int lane_off = 4 * grp * a.N;
+  asm volatile("" : "+v"(lane_off));
 #pragma unroll
   for (int g = 0; g < 8; ++g)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * g + 4 * grp + i;
-      if (r < rows) {
+      if (16 * g + 4 * grp + i < rows) {
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) o[r * a.N + 16 * j] = acc[g][j][i];   // < 2^31: r < 128, N <= 8192
+        for (int j = 0; j < SPW; ++j) o[lane_off + (16 * g + i) * a.N + 16 * j] = acc[g][j][i];   // < 2^31
       }
     }
 }

@@ -86,35 +86,53 @@ __device__ __forceinline__ void load_window(const uint32_t* __restrict__ tile, i
   lo = tile[b];
 }
 
+// A loaded window (raw words) prepared so that each of its eight 16-bit states (elements 8q ..
+// 8q+7) takes one or two instructions: for 4 bits the big-endian strings X = w[2q-1]:w[2q] and
+// L = w[2q]:w[2q+1] plus the raw low word, for other widths both words as big-endian strings.
+template <int BITS>
+struct Window {
+  uint32_t x, l, raw_lo;
+};
+
+template <int BITS>
+__device__ __forceinline__ Window<BITS> prep_window(uint32_t hi_raw, uint32_t lo_raw) {
+  Window<BITS> w;
+  if constexpr (BITS == 4) {
+    // words: hi_raw = w[2q-2] | w[2q-1] << 16, lo_raw = w[2q] | w[2q+1] << 16 (little endian)
+    w.x = __builtin_amdgcn_perm(hi_raw, lo_raw, 0x07060100u);   // bytes: lo.0 lo.1 hi.2 hi.3
+    w.l = be32(lo_raw);
+  } else {
+    w.x = be32(hi_raw);
+    w.l = be32(lo_raw);
+  }
+  w.raw_lo = lo_raw;
+  return w;
+}
+
+// State of element 8q+jj (jj a compile-time constant after unrolling).
+template <int BITS>
+__device__ __forceinline__ uint32_t window_state(const Window<BITS>& w, int q, int jj) {
+  if constexpr (BITS == 4) {
+    // the state of element 8q+j is the 16 stream bits ending at 4(8q+j+1): X >> (12-4j) for j < 3,
+    // L >> (28-4j) for 4 <= j < 7, and the raw half-words for j = 3 and 7
+    if (jj == 3) return w.raw_lo & 0xffffu;
+    if (jj == 7) return w.raw_lo >> 16;
+    return jj < 3 ? __builtin_amdgcn_ubfe(w.x, 12 - 4 * jj, 16) : __builtin_amdgcn_ubfe(w.l, 28 - 4 * jj, 16);
+  } else {
+    const int j0 = window_word<BITS>(q);
+    // element 8q+jj's state ends at stream bit (8q+jj+1)*BITS, i.e. end_rel bits into the window
+    const int shift = 64 - ((8 * q + jj + 1) * BITS - 32 * j0);
+    const uint32_t v = shift >= 32 ? (w.x >> (shift - 32)) : __builtin_amdgcn_alignbit(w.x, w.l, shift);
+    return v & 0xffffu;
+  }
+}
+
 // The 16-bit states of elements 8q .. 8q+7 from a loaded window (raw words).
 template <int BITS>
 __device__ __forceinline__ void window_states(uint32_t hi_raw, uint32_t lo_raw, int q, uint32_t (&st)[8]) {
-  if constexpr (BITS == 4) {
-    // words: hi_raw = w[2q-2] | w[2q-1] << 16, lo_raw = w[2q] | w[2q+1] << 16 (little endian).
-    // The state of element 8q+j is the 16 stream bits ending at 4(8q+j+1): with the big-endian
-    // strings X = w[2q-1]:w[2q] and L = w[2q]:w[2q+1] it is X >> (12-4j) for j < 3 and
-    // L >> (28-4j) for j >= 3, each masked to 16 bits.
-    const uint32_t X = __builtin_amdgcn_perm(hi_raw, lo_raw, 0x07060100u);   // bytes: lo.0 lo.1 hi.2 hi.3
-    const uint32_t L = be32(lo_raw);
-    st[0] = __builtin_amdgcn_ubfe(X, 12, 16);
-    st[1] = __builtin_amdgcn_ubfe(X, 8, 16);
-    st[2] = __builtin_amdgcn_ubfe(X, 4, 16);
-    st[3] = lo_raw & 0xffffu;
-    st[4] = __builtin_amdgcn_ubfe(L, 12, 16);
-    st[5] = __builtin_amdgcn_ubfe(L, 8, 16);
-    st[6] = __builtin_amdgcn_ubfe(L, 4, 16);
-    st[7] = lo_raw >> 16;
-  } else {
-    const uint32_t hi = be32(hi_raw), lo = be32(lo_raw);
-    const int j0 = window_word<BITS>(q);
+  const Window<BITS> w = prep_window<BITS>(hi_raw, lo_raw);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      // element 8q+jj's state ends at stream bit (8q+jj+1)*BITS, i.e. end_rel bits into the window
-      const int shift = 64 - ((8 * q + jj + 1) * BITS - 32 * j0);
-      const uint32_t w = shift >= 32 ? (hi >> (shift - 32)) : __builtin_amdgcn_alignbit(hi, lo, shift);
-      st[jj] = w & 0xffffu;
-    }
-  }
+  for (int jj = 0; jj < 8; ++jj) st[jj] = window_state<BITS>(w, q, jj);
 }
 
 // Decode elements 8q .. 8q+7 into four packed fp16 pairs (element 8q+2i in the low half of p[i]).

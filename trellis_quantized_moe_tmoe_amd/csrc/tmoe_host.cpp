@@ -158,7 +158,7 @@ struct GemmShape {          // launch shape of one grouped GEMM
 
 // Column groups, K steps, split bound and launch size of FC1 (fc = 1) or FC2 (fc = 2). For 16- to
 // 64-row tiles a unit is one wavefront's 64 columns and `waves` counts persistent wavefronts; for
-// 128-row tiles a unit is one workgroup's 128 columns and `waves` counts workgroups.
+// 128-row tiles a unit is one workgroup's 128 or 256 columns and `waves` counts workgroups.
 GemmShape gemm_shape(const tmoe_plan_s* p, long long R, int mg, bool fp8, int fc) {
   GemmShape g;
   const int K = fc == 1 ? p->H : p->I;
