@@ -161,7 +161,10 @@ __device__ __forceinline__ int owner_of(const int* tab, int E, int i) {
 
 // Expert totals given, one expert per thread: offsets, tile tables, expert table, scalars. Every
 // thread of the workgroup calls it (it holds workgroup barriers); returns this thread's expert
-// offset (0 for threads past E). The tile tables are written by all threads, one tile each in turn.
+// offset (0 for threads past E). With COOP the tile tables are written by all threads, one tile each
+// in turn (large batches, where one expert may hold hundreds of tiles); otherwise each expert's
+// thread writes its own few tiles.
+template <bool COOP>
 __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4* scan_smem, TableSmem& tb) {
   const int tid = threadIdx.x, E = a.num_experts;
   const bool own = tid < E;                      // E <= 512 < 1024: one expert per thread
@@ -179,16 +182,34 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
     info.bits = bits_e;
     info.pad = 0;
     a.einfo[tid] = info;
-    tb.off[tid] = off_e;
-    tb.toff[tid] = offs.y;
-    tb.goff[tid] = offs.z;
-    tb.boff[tid] = offs.w;
+    if constexpr (COOP) {
+      tb.off[tid] = off_e;
+      tb.toff[tid] = offs.y;
+      tb.goff[tid] = offs.z;
+      tb.boff[tid] = offs.w;
+    } else {
+      for (int t = 0; t < tiles_e; ++t) {
+        a.tile_expert[offs.y + t] = tid;
+        a.tile_row0[offs.y + t] = off_e + t * a.block_m;
+        a.tile_rows[offs.y + t] = min(a.block_m, total_e - t * a.block_m);
+      }
+      for (int t = 0; t < gtiles_e; ++t) {
+        int4 g;
+        g.x = tid | (bits_e << 24);
+        g.y = off_e + t * a.gemm_rows;
+        g.z = min(a.gemm_rows, total_e - t * a.gemm_rows);
+        g.w = static_cast<int>(info.word_offset >> 8);   // expert regions start on 256-word multiples
+        a.gtiles[offs.z + t] = g;
+      }
+    }
   }
   if (tid == 0) {
-    tb.off[E] = totals.x;
-    tb.toff[E] = totals.y;
-    tb.goff[E] = totals.z;
-    tb.boff[E] = totals.w;
+    if constexpr (COOP) {
+      tb.off[E] = totals.x;
+      tb.toff[E] = totals.y;
+      tb.goff[E] = totals.z;
+      tb.boff[E] = totals.w;
+    }
     a.offsets[E] = totals.x;
     *a.num_tiles = totals.y;
     *a.num_gtiles = totals.z;
@@ -196,6 +217,7 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
     a.splits[1] = a.nsplit[1];
     *a.status = bad;
   }
+  if constexpr (!COOP) return off_e;
   __syncthreads();
   for (int i = tid; i < totals.y; i += blockDim.x) {
     const int e = owner_of(tb.toff, E, i);
@@ -252,7 +274,7 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a, RotateArgs r
     for (int ww = 0; ww < kWaves; ++ww) total_e += cnt[ww * E + tid];
   if (tid == 0)
     for (int ww = 0; ww < kWaves; ++ww) bad += bad_w[ww];
-  const int off_e = publish_tables(a, total_e, bad, scan_smem, tb);
+  const int off_e = publish_tables<false>(a, total_e, bad, scan_smem, tb);
   if (tid < E) {                                 // per-wave starting slots
     int acc = off_e;
     for (int ww = 0; ww < kWaves; ++ww) {
@@ -353,7 +375,7 @@ __global__ __launch_bounds__(1024) void k_route_place(RouteMapArgs a) {
   __syncthreads();                               // cnt complete
   int off_e;
   if (g == 0) {
-    off_e = publish_tables(a, total_e, bad_all, scan_smem, tb);
+    off_e = publish_tables<true>(a, total_e, bad_all, scan_smem, tb);
   } else {
     int4 totals;
     off_e = block_exclusive_scan4(make_int4(tid < E ? total_e : 0, 0, 0, 0), scan_smem, &totals).x;

@@ -82,7 +82,7 @@ struct ActBody {
     for (int i = 0; i < S; ++i) {
       const float g = zg[i] * h2f(s1[64 * i]);
       const float u = zu[i] * h2f(s1[I + 64 * i]);
-      const float h = g / (1.0f + expf(-g)) * u;
+      const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;   // SiLU(g) * u
       bb[i] = h * h2f(s2[64 * i]);
     }
     if (!a.rot.identity) fwht_segment<S>(bb, lane);
