@@ -217,6 +217,8 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
     a.splits[1] = a.nsplit[1];
     *a.status = bad;
   }
+  // slots past the filled ones (dropped routes leave them empty) read as expert -1
+  for (int q = totals.x + tid; q < a.routes; q += blockDim.x) a.slot_expert[q] = -1;
   if constexpr (!COOP) return off_e;
   __syncthreads();
   for (int i = tid; i < totals.y; i += blockDim.x) {

@@ -104,9 +104,8 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (p >= a.routes) return;
-  const int filled = a.offsets[a.num_experts];   // both loads in flight together
-  const int e = a.slot_expert[p];                // (stale past the filled slots, unused there)
-  if (p >= filled) return;
+  const int e = a.slot_expert[p];                // -1 past the filled slots (dropped routes)
+  if (e < 0) return;
   ActBody<MX, SMAX> body{a, lane, p, e, a.rot.n, SMAX};
   for_segments<EPL>(a.rot, body);
 }
@@ -152,7 +151,22 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
     const int r = t * K + j;
     const int p = j < K ? a.route_slot[r] : -1;
     if (lane == 0) live[wv] = p >= 0;
-    if (p >= 0) {
+    if (p >= 0 && EPL > 0 && EPL <= 16) {
+      // power-of-two rows up to 1024: split sum, scale, rotation and weighting in registers, one
+      // LDS write of the finished row
+      constexpr int S = EPL > 0 && EPL <= 16 ? EPL : 1;
+      const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
+      const float wt = a.w[r];
+      float vv[S];
+      sum_splits<S, SMAX, splits_unroll<S, SMAX>(1)>(a.v + static_cast<size_t>(p) * H + lane, plane, splits, vv);
+      const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + lane;
+      const uint16_t* sg = a.sv2 + static_cast<size_t>(e) * H + lane;
+#pragma unroll
+      for (int i = 0; i < S; ++i) vv[i] *= h2f(c2[64 * i]);
+      if (!a.rot.identity) fwht_segment<S>(vv, lane);
+#pragma unroll
+      for (int i = 0; i < S; ++i) row[64 * i + lane] = wt * (vv[i] * h2f(sg[64 * i]));
+    } else if (p >= 0) {
       const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
       const float* src = a.v + static_cast<size_t>(p) * H + lane;
       const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + lane;

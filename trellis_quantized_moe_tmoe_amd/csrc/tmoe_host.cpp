@@ -251,7 +251,6 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
 
   const int32_t* sorted = at<int32_t>(scratch, p->lay.sorted);
   const int32_t* slot_expert = at<int32_t>(scratch, p->lay.slot_e);
-  const int32_t* offsets = at<int32_t>(scratch, p->lay.offsets);
   uint8_t* a1 = at<uint8_t>(scratch, p->lay.a1);
   uint8_t* a1s = a1 + static_cast<size_t>(R) * p->H;
   uint8_t* bq = at<uint8_t>(scratch, p->lay.b);
@@ -301,8 +300,6 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   aa.z = z;
   aa.nsplit = sh[0].most;
   aa.slot_expert = slot_expert;
-  aa.offsets = offsets;
-  aa.num_experts = p->E;
   aa.scale1 = wt->scale1;
   aa.sv1 = wt->sv1;
   aa.su2 = wt->su2;

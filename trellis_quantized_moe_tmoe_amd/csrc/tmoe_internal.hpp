@@ -28,7 +28,7 @@ struct RouteMapArgs {
   int32_t* num_gtiles;
   int32_t* splits;          // [2] K splits of FC1 and FC2, published for the consumers and tests
   int nsplit[2];            // the host's split counts
-  int32_t* slot_expert;     // [R]: expert of each slot
+  int32_t* slot_expert;     // [R]: expert of each slot, -1 past the filled slots
   int32_t* wg_counts;       // [workgroups][E + 1]: per-workgroup counts (large batches; E = invalid)
   ExpertInfo* einfo;
   uint32_t packed_bits[32]; // 2 bits per expert: bits - 2
@@ -61,9 +61,7 @@ struct RotateArgs {          // a = R_H(su1_e * x_t) per route, fp16 or MXFP8, r
 struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_I(z_u)))
   const float* z;            // [nsplit][R][2I] unscaled partial sums
   int nsplit;                // FC1 K splits: 1, 2, 4 or 8
-  const int32_t* slot_expert;
-  const int32_t* offsets;
-  int num_experts;
+  const int32_t* slot_expert;  // [R]: expert of each slot, -1 past the filled slots
   const uint16_t* scale1;    // [E][2I]
   const uint16_t* sv1;       // [E][2I]
   const uint16_t* su2;       // [E][I]
