@@ -260,6 +260,46 @@ def test_sampled_intermediates_prefill():
         assert np.max(np.abs(zz - tr["z"])) <= 5e-3 * np.max(np.abs(tr["z"]))
 
 
+def test_sampled_intermediates_w4a8():
+    """W4A8 at T = 64, sampled routes. (1) The stored MXFP8 rotated input, dequantized, against the
+    oracle's W4A8 trace (float64 rotation, then the same MXFP8 quantize-dequantize): the GPU rotates
+    in fp32, so a value within rounding distance of an E4M3 or scale boundary may land one step away;
+    everything else matches exactly. (2) FC1 of the same routes (E4M3 x E4M3 products summed in fp32)
+    against the trace, within what those one-step input differences can move it (|code| < 4)."""
+    from trellis_quantized_moe_tmoe_amd.layer import scratch_view
+    c = Case("w4a8", 64)
+    c.run(w4a8=True)
+    view = c.plan.debug_views(c.inp.tokens, True, c.scratch)
+    R, H, I = c.inp.routes, c.inp.hidden, c.inp.inter
+    assert view.a1_pitch == H
+    q = scratch_view(c.scratch, view.a1, (R, H), torch.uint8).cpu().numpy()
+    sc = scratch_view(c.scratch, view.a1_scale, (R, H // 32), torch.uint8).cpu().numpy()
+    splits1 = int(scratch_view(c.scratch, view.splits, (2,), torch.int32)[0].item())
+    z = scratch_view(c.scratch, view.z, (splits1, R, 2 * I), torch.float32).clone()
+    slots = c.plan.route_map(c.ids, c.scratch)
+    torch.cuda.synchronize()
+    route_slot = scratch_view(c.scratch, slots.route_slot, (R,), torch.int32).cpu().numpy()
+    lib = O.lib()
+    e4m3 = np.array([lib.orc_e4m3_to_double(b) for b in range(256)])
+    rng = np.random.default_rng(1)
+    exact = total = 0
+    for r in rng.choice(R, size=16, replace=False):
+        t, j = divmod(int(r), c.inp.top_k)
+        tr = O.route_trace(c.inp, t, j, mode="w4a8")
+        blk = np.repeat(np.exp2(sc[r].astype(np.float64) - 127), 32)
+        got = e4m3[q[r]] * blk
+        want = tr["a"]
+        exact += int(np.sum(got == want))
+        total += H
+        assert np.all(np.abs(got - want) <= 0.13 * np.abs(want) + 2.0 ** -9 * blk)
+        e = int(c.inp.ids[t, j])
+        zz = z[:, int(route_slot[r])].double().sum(0).cpu().numpy() * c.inp.scale1[e].astype(np.float64)
+        moved = 4.0 * np.sum(np.abs(got - want)) * np.max(np.abs(c.inp.scale1[e].astype(np.float64)))
+        assert np.max(np.abs(zz - tr["z"])) <= 1e-4 * np.max(np.abs(tr["z"])) + moved   # fp32 sums over K
+    say(f"[result] {c.label} W4A8 A1: {exact}/{total} dequantized values exact")
+    assert exact >= 0.999 * total
+
+
 def test_graph_capture_replay_with_changed_inputs():
     c = Case("decode", 16)
     y = torch.empty((16, c.inp.hidden), device="cuda")
