@@ -139,6 +139,18 @@ def test_layer_w4a16_shape_edges(over):
     assert err <= TOL_W4A16
 
 
+@pytest.mark.parametrize("T", [4, 2100])
+def test_layer_w4a16_block_rows_split_and_whole(T):
+    # H = 192 and I = 320 rotate as 128 + 64 blocks. T = 4: rotation and combine split rows into
+    # blocks (one wavefront / workgroup each); T = 2100 (10500 routes): whole rows per wavefront and
+    # per token, with a row length that is not a multiple of the 512-value staging chunk.
+    c = Case("tiny", T, hidden=192, inter=320, experts=5, top_k=5)
+    y = c.run().cpu().numpy()
+    err = rel_err(y, c.oracle_w4a16)
+    say(f"[result] {c.label} W4A16 rel err {err:.3e}")
+    assert err <= TOL_W4A16
+
+
 @pytest.mark.parametrize("T", [40, 64, 200])
 def test_layer_w4a16_workgroup_tiles_with_k_splits(T):
     # 2T routes over 8 experts: 128-row workgroup tiles, with 4, 4 and 2 K splits

@@ -245,7 +245,7 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
 }
 
 // All routes in one workgroup (workgroup 0): each wave takes a contiguous segment of R/16 routes.
-// Workgroups 1.. rotate the input rows, 16 routes each (ROT = false: none).
+// Workgroups 1.. rotate the input rows, 16 items each (ROT = false: none).
 template <bool ROT, int EPL, bool MX>
 __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a, RotateArgs ra) {
   if constexpr (ROT) {
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(1024) void k_route_map(RouteMapArgs a, RotateArgs r
 
 // Large batches, launch 1 of 2: workgroup g counts routes [g * kRouteChunk, (g + 1) * kRouteChunk)
 // per expert into wg_counts[g][0..E) and its invalid ids into wg_counts[g][E]. Workgroups past the
-// counting ones rotate the input rows, 16 routes each.
+// counting ones rotate the input rows, 16 items each.
 template <bool ROT, int EPL, bool MX>
 __global__ __launch_bounds__(1024) void k_route_count(RouteMapArgs a, RotateArgs ra, int count_groups) {
   if constexpr (ROT) {
@@ -395,7 +395,9 @@ __global__ __launch_bounds__(1024) void k_route_place(RouteMapArgs a) {
 }
 
 void launch_route_map(const RouteMapArgs& a, const RotateArgs* ra, bool mx, hipStream_t s) {
-  const unsigned rot_groups = ra ? static_cast<unsigned>((ra->routes + kWaves - 1) / kWaves) : 0;
+  // rotation workgroups: one wavefront per route or per (route, row segment)
+  const long long rot_items = ra ? static_cast<long long>(ra->routes) * rotate_items_per_route(*ra) : 0;
+  const unsigned rot_groups = static_cast<unsigned>((rot_items + kWaves - 1) / kWaves);
   const RotateArgs none{};
   const RotateArgs& r = ra ? *ra : none;
   auto go = [&](auto rot, auto epl, auto m) {

@@ -99,15 +99,19 @@ struct ActBody {
   }
 };
 
+// One wavefront per (slot, row segment): every step of the epilogue (rotations, SiLU, scales) stays
+// inside one segment of the intermediate row.
 template <int EPL, bool MX, int SMAX>
 __global__ __launch_bounds__(256) void k_act(ActArgs a) {
   const int lane = threadIdx.x & 63;
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nseg = EPL > 0 ? 1 : row_segments(a.rot);
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int p = item / nseg, seg = item - p * nseg;
   if (p >= a.routes) return;
   const int e = a.slot_expert[p];                // -1 past the filled slots (dropped routes)
   if (e < 0) return;
   ActBody<MX, SMAX> body{a, lane, p, e, a.rot.n, SMAX};
-  for_segments<EPL>(a.rot, body);
+  run_segment<EPL>(a.rot, seg, body);
 }
 
 // Rotates one route's row held in LDS in place: o = wt * sv2_e * R_H(row).
@@ -128,21 +132,27 @@ struct CombineRotBody {
   }
 };
 
-// One workgroup of W wavefronts per token t. Round it handles routes j = it * W + w (wavefront w):
-// the split sum of v times scale2 is staged in the wavefront's LDS row, rotated there, weighted;
-// after a barrier every thread adds its columns of the W rows in ascending j onto a running sum
-// kept in LDS (the last round writes y instead). Dropped routes add nothing. LDS: (W + 1) * H floats
-// plus W flags.
+// One workgroup of W wavefronts per token t, or (split_segments, few tokens with a long
+// non-power-of-two row) per (token, row segment): one 128-value block or the 64-value tail, as the
+// rotation never crosses a segment.
+// Round it handles routes j = it * W + w (wavefront w): the split sum of v times scale2, rotated,
+// times sv2 and the route's weight, goes to the wavefront's LDS row (in registers up to 16 values
+// per lane; longer rows are staged in LDS and rotated there); after a barrier every thread adds its
+// columns of the W rows in ascending j onto a running sum kept in LDS (the last round writes y
+// instead). Dropped routes add nothing. LDS: (W + 1) * L floats plus W flags, L the segment length.
 template <int EPL, int SMAX>
 __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs a) {
   extern __shared__ float lds[];
   const int H = a.rot.n, K = a.top_k;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, W = blockDim.x >> 6;
-  const int t = blockIdx.x;
-  float* acc = lds;                         // [H]
-  float* rows = lds + H;                    // [W][H]
-  int* live = reinterpret_cast<int*>(rows + static_cast<size_t>(W) * H);   // [W]
-  float* row = rows + static_cast<size_t>(wv) * H;
+  const int t = blockIdx.x, seg = blockIdx.y;
+  const bool split = EPL == 0 && a.split_segments;
+  const int off = split ? seg * 128 : 0;
+  const int L = !split ? H : (seg < a.rot.nblk128 ? 128 : 64);
+  float* acc = lds;                         // [L]
+  float* rows = lds + L;                    // [W][L]
+  int* live = reinterpret_cast<int*>(rows + static_cast<size_t>(W) * L);   // [W]
+  float* row = rows + static_cast<size_t>(wv) * L;
   const int splits = SMAX;
   const size_t plane = static_cast<size_t>(a.routes) * H;
   const int rounds = (K + W - 1) / W;
@@ -151,58 +161,64 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
     const int r = t * K + j;
     const int p = j < K ? a.route_slot[r] : -1;
     if (lane == 0) live[wv] = p >= 0;
-    if (p >= 0 && EPL > 0 && EPL <= 16) {
-      // power-of-two rows up to 1024: split sum, scale, rotation and weighting in registers, one
-      // LDS write of the finished row
-      constexpr int S = EPL > 0 && EPL <= 16 ? EPL : 1;
+    if (p >= 0) {
       const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
-      const float wt = a.w[r];
-      float vv[S];
-      sum_splits<S, SMAX, splits_unroll<S, SMAX>(1)>(a.v + static_cast<size_t>(p) * H + lane, plane, splits, vv);
-      const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + lane;
-      const uint16_t* sg = a.sv2 + static_cast<size_t>(e) * H + lane;
+      // S values per lane in registers: split sum, scale, rotation, sign and weight, one LDS write
+      auto in_registers = [&](auto s_const) {
+        constexpr int S = decltype(s_const)::value;
+        const float wt = a.w[r];
+        float vv[S];
+        sum_splits<S, SMAX, splits_unroll<S, SMAX>(1)>(a.v + static_cast<size_t>(p) * H + off + lane, plane, splits, vv);
+        const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + off + lane;
+        const uint16_t* sg = a.sv2 + static_cast<size_t>(e) * H + off + lane;
 #pragma unroll
-      for (int i = 0; i < S; ++i) vv[i] *= h2f(c2[64 * i]);
-      if (!a.rot.identity) fwht_segment<S>(vv, lane);
+        for (int i = 0; i < S; ++i) vv[i] *= h2f(c2[64 * i]);
+        if (!a.rot.identity) fwht_segment<S>(vv, lane);
 #pragma unroll
-      for (int i = 0; i < S; ++i) row[64 * i + lane] = wt * (vv[i] * h2f(sg[64 * i]));
-    } else if (p >= 0) {
-      const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
-      const float* src = a.v + static_cast<size_t>(p) * H + lane;
-      const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + lane;
-      constexpr int U = 8;
-      for (int base = 0; base < H; base += 64 * U) {
-        float sum[U];
-        if (base + 64 * U <= H) {
-          sum_splits<U, SMAX, splits_unroll<U, SMAX>(1)>(src + base, plane, splits, sum);
+        for (int i = 0; i < S; ++i) row[64 * i + lane] = wt * (vv[i] * h2f(sg[64 * i]));
+      };
+      if (split) {
+        if (L == 128) in_registers(std::integral_constant<int, 2>{});
+        else in_registers(std::integral_constant<int, 1>{});
+      } else if constexpr (EPL > 0 && EPL <= 16) {
+        in_registers(std::integral_constant<int, EPL>{});
+      } else {
+        const float* src = a.v + static_cast<size_t>(p) * H + lane;
+        const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + lane;
+        constexpr int U = 8;
+        for (int base = 0; base < H; base += 64 * U) {
+          if (base + 64 * U <= H) {
+            float sum[U];
+            sum_splits<U, SMAX, splits_unroll<U, SMAX>(1)>(src + base, plane, splits, sum);
 #pragma unroll
-          for (int i = 0; i < U; ++i) row[base + 64 * i + lane] = sum[i] * h2f(c2[base + 64 * i]);
-        } else {
-          for (int c = base; c < H; c += 64) {
-            float one[1];
-            sum_splits<1, SMAX, SMAX>(src + c, plane, splits, one);
-            row[c + lane] = one[0] * h2f(c2[c]);
+            for (int i = 0; i < U; ++i) row[base + 64 * i + lane] = sum[i] * h2f(c2[base + 64 * i]);
+          } else {
+            for (int c = base; c < H; c += 64) {
+              float one[1];
+              sum_splits<1, SMAX, SMAX>(src + c, plane, splits, one);
+              row[c + lane] = one[0] * h2f(c2[c]);
+            }
           }
         }
+        CombineRotBody body{a, row, lane, e, a.w[r]};
+        for_segments<EPL>(a.rot, body);
       }
-      CombineRotBody body{a, row, lane, e, a.w[r]};
-      for_segments<EPL>(a.rot, body);
     }
     __syncthreads();
-    const int H4 = H >> 2;
+    const int L4 = L >> 2;
     const bool last = it + 1 == rounds;
     const int nw = K - it * W < W ? K - it * W : W;
-    for (int c = threadIdx.x; c < H4; c += blockDim.x) {
+    for (int c = threadIdx.x; c < L4; c += blockDim.x) {
       float4 s4 = it == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : reinterpret_cast<const float4*>(acc)[c];
       for (int w = 0; w < nw; ++w) {
         if (!live[w]) continue;
-        const float4 x = reinterpret_cast<const float4*>(rows + static_cast<size_t>(w) * H)[c];
+        const float4 x = reinterpret_cast<const float4*>(rows + static_cast<size_t>(w) * L)[c];
         s4.x += x.x;
         s4.y += x.y;
         s4.z += x.z;
         s4.w += x.w;
       }
-      if (last) reinterpret_cast<float4*>(a.y + static_cast<size_t>(t) * H)[c] = s4;
+      if (last) reinterpret_cast<float4*>(a.y + static_cast<size_t>(t) * H + off)[c] = s4;
       else reinterpret_cast<float4*>(acc)[c] = s4;
     }
     __syncthreads();
@@ -283,22 +299,26 @@ int combine_waves(int hidden, int top_k) {
 }  // namespace
 
 void launch_act(const ActArgs& a, bool mx, hipStream_t s) {
+  const unsigned grid = blocks_for(static_cast<long long>(a.routes) * row_segments(a.rot));
   dispatch_epl(a.rot, [&](auto epl) {
     dispatch_smax(a.nsplit, [&](auto sm) {
       constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;
-      if (mx) hipLaunchKernelGGL((k_act<E, true, SM>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((k_act<E, false, SM>), dim3(blocks_for(a.routes)), dim3(256), 0, s, a);
+      if (mx) hipLaunchKernelGGL((k_act<E, true, SM>), dim3(grid), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_act<E, false, SM>), dim3(grid), dim3(256), 0, s, a);
     });
   });
 }
 
 void launch_combine(const CombineArgs& a, hipStream_t s) {
-  const int W = combine_waves(a.rot.n, a.top_k);
-  const size_t lds = static_cast<size_t>(W + 1) * a.rot.n * 4 + 4 * W;
+  const bool split = !a.rot.pow2 && a.split_segments;
+  const int L = split ? 128 : a.rot.n;           // longest segment a workgroup combines
+  const int W = combine_waves(L, a.top_k);
+  const size_t lds = static_cast<size_t>(W + 1) * L * 4 + 4 * W;
+  const dim3 grid(a.tokens, split ? row_segments(a.rot) : 1);
   dispatch_epl(a.rot, [&](auto epl) {
     dispatch_smax(a.nsplit, [&](auto sm) {
       constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;
-      hipLaunchKernelGGL((k_combine<E, SM>), dim3(a.tokens), dim3(64 * W), lds, s, a);
+      hipLaunchKernelGGL((k_combine<E, SM>), grid, dim3(64 * W), lds, s, a);
     });
   });
 }

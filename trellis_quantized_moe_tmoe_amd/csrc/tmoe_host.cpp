@@ -270,6 +270,9 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   ra.a1_scale = a1s;
   ra.lda = fp16_pitch(p->H);
   ra.routes = static_cast<int>(R);
+  // rows of a non-power-of-two length split into their 128-blocks while the routes alone would not
+  // fill the chip; with many routes one wavefront per route keeps its loads better in flight
+  ra.split_segments = R < 2048 ? 1 : 0;
 
   (void)hipGetLastError();   // clear a stale error so the check below reports this call only
   auto on = [&](int stage) { return first <= stage && stage <= last; };
@@ -340,6 +343,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   ca.sv2 = wt->sv2;
   ca.rot = make_rot(p->H, p->rotation == TMOE_ROT_IDENTITY);
   ca.y = y;
+  ca.split_segments = static_cast<long long>(T) * make_rot(p->H, 0).nblk128 <= 2048 ? 1 : 0;
   if (on(4)) launch_combine(ca, s);
 
   return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;

@@ -56,6 +56,7 @@ struct RotateArgs {          // a = R_H(su1_e * x_t) per route, fp16 or MXFP8, r
   uint8_t* a1_scale;         // [R][H/32]
   int lda;                   // fp16 row pitch in elements (>= H)
   int routes;
+  int split_segments;        // non-power-of-two H: one wavefront per (route, 128-block) instead of per route
 };
 
 struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_I(z_u)))
@@ -86,6 +87,7 @@ struct CombineArgs {         // y_t = sum_j w[t,j] * sv2_e * R_H(scale2_e * v_sl
   const uint16_t* sv2;       // [E][H]
   RowRot rot;                // n = H
   float* y;                  // [T][H]
+  int split_segments;        // non-power-of-two H: one workgroup per (token, 128-block) instead of per token
 };
 
 struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slot][k] * C_e[k][n]

@@ -22,6 +22,23 @@ __device__ __forceinline__ void for_segments(const RowRot& rot, Body& body) {
   }
 }
 
+// Segments of a row that rotate independently: the whole row for a power-of-two length, else its
+// 128-value blocks and the 64-value tail. Row kernels give each segment a wavefront of its own, so a
+// long non-power-of-two row is not walked block after block by one wavefront.
+__host__ __device__ inline int row_segments(const RowRot& rot) { return rot.pow2 ? 1 : rot.nblk128 + rot.tail64; }
+
+// Run body on segment seg of the row (EPL > 0: the whole row, EPL values per lane; EPL = 0: block
+// seg, 2 values per lane, or the 64-value tail, 1 per lane).
+template <int EPL, class Body>
+__device__ __forceinline__ void run_segment(const RowRot& rot, int seg, Body& body) {
+  if constexpr (EPL > 0) {
+    body.template run<EPL>(0);
+  } else {
+    if (seg < rot.nblk128) body.template run<2>(seg * 128);
+    else body.template run<1>(rot.nblk128 * 128);
+  }
+}
+
 // MXFP8 of one value per lane; each 32-lane half of the wavefront is one 32-value block.
 __device__ __forceinline__ void mx_store(float v, int lane, uint8_t* q_row, uint8_t* s_row, int idx) {
   const float amax = half_wave_amax(v);
@@ -73,17 +90,26 @@ void dispatch_epl(const RowRot& rot, F&& f) {
   }
 }
 
-// Workgroup-level input rotation, one route per wavefront: route r = first + wave. Used by the
-// route-map launch for its extra workgroups (the rotation does not depend on the route map).
+// Items of the input rotation: routes, or (route, row segment) pairs when the host splits rows (few
+// routes with long non-power-of-two rows).
+__host__ __device__ inline int rotate_items_per_route(const RotateArgs& a) {
+  return a.split_segments ? row_segments(a.rot) : 1;
+}
+
+// Workgroup-level input rotation, one item per wavefront: item first + wave. Used by the route-map
+// launch for its extra workgroups (the rotation does not depend on the route map).
 template <int EPL, bool MX>
 __device__ __forceinline__ void rotate_routes(const RotateArgs& a, int first) {
   const int lane = threadIdx.x & 63;
-  const int r = first + static_cast<int>(threadIdx.x >> 6);
+  const int per = EPL > 0 ? 1 : rotate_items_per_route(a);
+  const int item = first + static_cast<int>(threadIdx.x >> 6);
+  const int r = item / per, seg = item - r * per;
   if (r >= a.routes) return;
   const long long e = route_expert(a.ids, a.ids64, r);
   if (e < 0 || e >= a.num_experts) return;         // dropped route: its row is never read
   RotateBody<MX> body{a, lane, r, r / a.top_k, static_cast<int>(e), a.rot.n};
-  for_segments<EPL>(a.rot, body);
+  if (per > 1) run_segment<EPL>(a.rot, seg, body);
+  else for_segments<EPL>(a.rot, body);
 }
 
 }  // namespace tmoe
