@@ -1,8 +1,10 @@
-// k_route_map.hip -- stable token-major route map in one workgroup.
+// k_route_map.hip -- stable token-major route map: one workgroup up to 4096 routes, else a count
+// launch and a placement launch over 1024-route chunks; the same launch carries the input rotation.
 //
 // The route map is materialised once and consumed directly by FC1 and FC2 ("serve canonical Fruit
 // QSRT atoms", Hot path); per-expert counts and an exclusive prefix give expert offsets and routed
-// blocks (sparkinfer PR #90, review of route_pack.py). Stable token-major order within an expert
+// blocks ("integrate EXL3 Trellis into the fused W4A16 API", review of route_pack.py). Stable
+// token-major order within an expert
 // follows the O(routes + experts * tiles) stable design asked for in the review of route_pack.py
 // on "Share trellis preparation across native and EXL3 containers": the routes are walked once per
 // pass in wave-sized chunks, and per-wave, per-expert running positions replace any rescan.

@@ -1,13 +1,14 @@
-// k_rowops.hip -- per-row kernels around the two trellis GEMMs, one wavefront per row.
+// k_rowops.hip -- per-row kernels around the two trellis GEMMs.
 //
 //  (the input rotation runs in the route-map launch, k_route_map.hip)
 //  k_act    : the activation epilogue between FC1 and FC2 in the pages' order
 //             R_I -> svh -> silu(gate) * up -> suh_down -> R_I ("integrate EXL3 Trellis into the
-//             fused W4A16 API", review of kernel.py), with the FC1 channel scales applied first.
+//             fused W4A16 API", review of kernel.py), with the FC1 channel scales applied first;
+//             one wavefront per slot, or per (slot, 128-block) for rows rotated in blocks.
 //  k_combine: y_t = sum over j ascending of w[t,j] * sv2_e * R_H(scale2_e * v), the output rotation
-//             with exact top-k weighting. One workgroup per token: each wavefront rotates one of the
-//             token's routes into LDS, then every column is summed in ascending j with no atomics,
-//             so repeated calls are bitwise identical.
+//             with exact top-k weighting. One workgroup per token (or per (token, 128-block)): each
+//             wavefront rotates one of the token's routes into LDS, then every column is summed in
+//             ascending j with no atomics, so repeated calls are bitwise identical.
 //
 // The FC1/FC2 GEMMs leave up to 8 K-split partial planes; every reader sums them in ascending split
 // order, with all loads of a row issued before the first add so one memory latency covers them.

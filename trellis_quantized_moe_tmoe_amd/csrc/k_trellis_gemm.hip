@@ -7,10 +7,12 @@
 // plane per K split, summed in a fixed order by the consumer kernel (deterministic; no atomics).
 //
 // Work unit of one wavefront: (GEMM tile = expert + up to 16*MG slots, 64 output columns, one K
-// split). Units are dealt round-robin to a persistent grid whose size is fixed on the host, so the
-// launch is graph-capturable although the tile count is only known on the device. Within a unit
-// the payload words and activation fragments of the next D steps are kept in flight in a register
-// ring, so decode of step k overlaps the memory latency of steps k+1 .. k+D.
+// split); the large-batch kernel's unit is a workgroup's (128-slot tile, 256 columns, K split).
+// Units are dealt to a persistent grid whose size is fixed on the host, so the launch is
+// graph-capturable although the tile count is only known on the device. Within a unit the payload
+// words and activation fragments of the next steps are kept in flight in an LDS ring filled by
+// direct global->LDS loads (the fp16 kernels) or in registers (the fp8 kernel), so the decode of
+// one step overlaps the memory latency of the next ones.
 //
 // Operand layouts (gfx950, checked on hardware):
 //  * v_mfma_f32_16x16x32_f16: A lane l = row l%16, k = 8*(l/16)+[0,8); B lane l = column l%16,
