@@ -46,6 +46,10 @@ RowRot make_rot(int n, int identity) {
 // the K steps so every split has the same depth.
 int choose_splits(long long routes, int ksteps) {
   int target = routes <= 32 ? 8 : routes <= 128 ? 4 : routes <= 512 ? 2 : 1;
+  // small batches with a deep K (long rows): also keep a unit at about ten K steps, so every SIMD
+  // still gets several short units (wide geometry FC1: 61 -> 44 us at T = 16)
+  if (routes <= 512)
+    while (target < 8 && ksteps > 10 * target) target *= 2;
   for (int s = target; s > 1; s >>= 1)
     if (ksteps % s == 0) return s;
   return 1;
