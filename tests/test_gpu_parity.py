@@ -190,6 +190,30 @@ def test_w4a8_tiny():
     assert err <= TOL_W4A8_EMU
 
 
+def test_scales_and_signs_at_two_byte_alignment():
+    """fp16 scale and sign vectors one element past a 16-byte boundary (the ABI asks only 2-byte
+    alignment): the row kernels take their strided loads instead of 16-byte ones, same result."""
+    c = Case("decode", 16)
+    ref = c.run().clone()
+    W = c.L.DeviceWeights
+    shifted = []
+    for n in W.FIELDS:
+        t = getattr(c.weights, n)
+        if n != "payload":
+            buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+            buf[1:1 + t.numel()] = t.reshape(-1)
+            t = buf[1:1 + t.numel()].view(t.shape)
+            assert t.data_ptr() % 16 == 2
+        shifted.append(t)
+    c.weights = W(*shifted)
+    y = c.run()
+    err = rel_err(y.cpu().numpy(), c.oracle_w4a16)
+    say(f"[result] {c.label} shifted scales rel err {err:.3e}")
+    assert err <= TOL_W4A16
+    # the two layouts run the butterfly stages in another order: fp32 rounding, and the odd fp16 step
+    assert torch.allclose(y, ref, rtol=0, atol=2e-4 * float(ref.abs().max()))
+
+
 @pytest.mark.parametrize("w4a8", [False, True])
 def test_identity_rotation_mode(w4a8):
     c = Case("tiny", 4, rotation="identity", identity_signs=True)

@@ -54,12 +54,60 @@ constexpr int splits_unroll(int rows) {   // planes loaded per round: about 64 l
   return SMAX * S * rows <= 64 ? SMAX : (64 / (S * rows) >= 1 ? 64 / (S * rows) : 1);
 }
 
+// Values of a lane: elements off + 64 i + lane (strided), or for fp16 rows with 8 or more values per
+// lane whose scale and sign vectors are 16-byte aligned, off + S lane + i (blocked: 16-byte loads and
+// stores; the butterflies cover every index bit either way).
+template <int S>
+__device__ __forceinline__ void load_f16_blocked(const uint16_t* src, float (&out)[S]) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int c = 0; c < S / 8; ++c) {
+    const h8 v = reinterpret_cast<const h8*>(src)[c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[8 * c + i] = static_cast<float>(v[i]);
+  }
+}
+
+// sum_splits for the blocked layout of the activation: out[i] = sum over s < SMAX, ascending, of
+// src[s * plane + i] (src already at the lane's S values, 16-byte aligned).
+template <int S, int SMAX, int SU>
+__device__ __forceinline__ void sum_splits_blocked(const float* __restrict__ src, size_t plane, float (&out)[S]) {
+  static_assert(SMAX % SU == 0, "split rounds");
+#pragma unroll
+  for (int i = 0; i < S; ++i) out[i] = 0.0f;
+#pragma unroll 1
+  for (int s0 = 0; s0 < SMAX; s0 += SU) {
+    float4 t[SU][S / 4];
+#pragma unroll
+    for (int u = 0; u < SU; ++u)
+#pragma unroll
+      for (int c = 0; c < S / 4; ++c) t[u][c] = reinterpret_cast<const float4*>(src + (s0 + u) * plane)[c];
+#pragma unroll
+    for (int u = 0; u < SU; ++u)
+#pragma unroll
+      for (int c = 0; c < S / 4; ++c) {
+        out[4 * c] += t[u][c].x;
+        out[4 * c + 1] += t[u][c].y;
+        out[4 * c + 2] += t[u][c].z;
+        out[4 * c + 3] += t[u][c].w;
+      }
+  }
+}
+
+__device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 template <bool MX, int SMAX>
 struct ActBody {
   const ActArgs& a;
   int lane, p, e, I, splits;
   template <int S>
   __device__ __forceinline__ void run(int off) {
+    if constexpr (!MX && S >= 8) {
+      if (aligned16(a.scale1) && aligned16(a.sv1) && aligned16(a.su2)) {
+        run_blocked<S>(off);
+        return;
+      }
+    }
     float zg[S], zu[S];
     const size_t plane = static_cast<size_t>(a.routes) * 2 * I;
     const float* zr = a.z + static_cast<size_t>(p) * 2 * I + off + lane;
@@ -96,6 +144,48 @@ struct ActBody {
       uint8_t* sc = a.b_scale + static_cast<size_t>(p) * (I / 32);
 #pragma unroll
       for (int i = 0; i < S; ++i) mx_store(bb[i], lane, q, sc, off + 64 * i + lane);
+    }
+  }
+  template <int S>
+  __device__ __forceinline__ void run_blocked(int off) {
+    const size_t plane = static_cast<size_t>(a.routes) * 2 * I;
+    const float* zr = a.z + static_cast<size_t>(p) * 2 * I + off + S * lane;
+    float zg[S], zu[S];
+    sum_splits_blocked<S, SMAX, splits_unroll<S, SMAX>(2)>(zr, plane, zg);
+    sum_splits_blocked<S, SMAX, splits_unroll<S, SMAX>(2)>(zr + I, plane, zu);
+    const size_t erow = static_cast<size_t>(e) * 2 * I + off + S * lane;
+    float cg[S], cu[S], sg[S], su[S], s2[S];
+    load_f16_blocked<S>(a.scale1 + erow, cg);
+    load_f16_blocked<S>(a.scale1 + erow + I, cu);
+    load_f16_blocked<S>(a.sv1 + erow, sg);
+    load_f16_blocked<S>(a.sv1 + erow + I, su);
+    load_f16_blocked<S>(a.su2 + static_cast<size_t>(e) * I + off + S * lane, s2);
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      zg[i] *= cg[i];
+      zu[i] *= cu[i];
+    }
+    if (!a.rot.identity) {
+      fwht_segment<S>(zg, lane);
+      fwht_segment<S>(zu, lane);
+    }
+    float bb[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const float g = zg[i] * sg[i];
+      const float u = zu[i] * su[i];
+      const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;   // SiLU(g) * u
+      bb[i] = h * s2[i];
+    }
+    if (!a.rot.identity) fwht_segment<S>(bb, lane);
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    h8* out = reinterpret_cast<h8*>(static_cast<_Float16*>(a.b) + static_cast<size_t>(p) * a.ldb + off + S * lane);
+#pragma unroll
+    for (int c = 0; c < S / 8; ++c) {
+      h8 o;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(bb[8 * c + i]);
+      out[c] = o;
     }
   }
 };

@@ -50,6 +50,10 @@ __device__ __forceinline__ void mx_store(float v, int lane, uint8_t* q_row, uint
 }
 
 // Input rotation of one route (token t, expert e): a = R_H(su1_e * x_t) into operand row p.
+// The butterflies of fwht_segment act on every bit of the element index, so the transform is the
+// same whether a lane holds elements off + 64 i + lane (strided) or off + S lane + i (blocked); the
+// fp16 path with 8 or more values per lane uses the blocked layout, whose loads and stores are 16
+// bytes wide (MXFP8 keeps the strided one: its 32-value blocks are half-wavefronts there).
 template <bool MX>
 struct RotateBody {
   const RotateArgs& a;
@@ -57,6 +61,31 @@ struct RotateBody {
   template <int S>
   __device__ __forceinline__ void run(int off) {
     float v[S];
+    // (the signs need only 2-byte alignment by contract; x and the arena are 16-byte aligned)
+    if constexpr (!MX && S >= 8) {
+      if ((reinterpret_cast<uintptr_t>(a.su1) & 15) == 0) {
+        typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        const u16x8* xr = reinterpret_cast<const u16x8*>(a.x + static_cast<size_t>(t) * H + off + S * lane);
+        const u16x8* sr = reinterpret_cast<const u16x8*>(a.su1 + static_cast<size_t>(e) * H + off + S * lane);
+#pragma unroll
+        for (int c = 0; c < S / 8; ++c) {
+          const u16x8 xv = xr[c], sv = sr[c];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[8 * c + i] = bf16_to_f32(xv[i]) * h2f(sv[i]);
+        }
+        if (!a.rot.identity) fwht_segment<S>(v, lane);
+        h8* out = reinterpret_cast<h8*>(static_cast<_Float16*>(a.a1) + static_cast<size_t>(p) * a.lda + off + S * lane);
+#pragma unroll
+        for (int c = 0; c < S / 8; ++c) {
+          h8 o;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(v[8 * c + i]);
+          out[c] = o;
+        }
+        return;
+      }
+    }
     const uint16_t* xr = a.x + static_cast<size_t>(t) * H + off + lane;
     const uint16_t* sr = a.su1 + static_cast<size_t>(e) * H + off + lane;
 #pragma unroll
