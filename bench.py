@@ -11,7 +11,9 @@ Timing: the K steps are captured into one hipGraph and replayed between two even
 stream. Per-stage durations come from K more forwards issued stage by stage with events between
 the stages on the same stream, queued behind a bounded spin kernel so the GPU runs them back to
 back. The dominant kernel's average duration (for the roofline figure) comes from K back-to-back
-launches of that kernel alone between two events, also queued behind the spin kernel.
+launches of that kernel alone between two events, also queued behind the spin kernel. The
+per-forward distribution (median, p10, p90) comes from 200 replays of one-forward graphs, one graph
+per weight copy, after 20 untimed replays.
 
 Prints one JSON line.
 """
@@ -37,6 +39,8 @@ COPY_FOOTPRINT = 1.0e9
 # Stored FETCH_SIZE / WRITE_SIZE counters of the headline kernel and the sources they were taken with
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_f16_small_fc1_decode_T16_traffic.txt")
 TRAFFIC_SOURCES = ["k_trellis_gemm.hip", "tmoe_device.hpp", "tmoe_internal.hpp", "tmoe_host.cpp"]
+# Stored VALU / MFMA activity counters of the GEMM kernels (same source hash)
+BUSY_FILE = os.path.join(ROOT, "profiles", "gemm_valu_mfma_busy.txt")
 
 
 def parse():
@@ -153,6 +157,42 @@ class Bench:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    def _replay_stats(self, replays: int = 200, warm: int = 20) -> dict:
+        """Per-forward distribution: one graph per weight copy, each holding one forward; `warm`
+        untimed replays, then `replays` replays cycling the copies, each between two events, all
+        queued behind a bounded spin kernel so the events see GPU time. Microseconds."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        with torch.cuda.stream(s):
+            self.forward(0)
+        torch.cuda.synchronize()
+        for c in range(self.n_copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                self.forward(c)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(warm):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+        hold_s = 0.2
+        torch.cuda._sleep(int(hold_s * 2.4e9))
+        t0 = time.perf_counter()
+        for i in range(replays):
+            ev[i][0].record()
+            graphs[i % len(graphs)].replay()
+            ev[i][1].record()
+        enqueue_s = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        del graphs
+        return {"median": float(np.median(us)), "p10": float(np.percentile(us, 10)),
+                "p90": float(np.percentile(us, 90)), "replays": replays, "warmup_replays": warm,
+                "graphs": self.n_copies, "enqueued_within_hold": bool(enqueue_s < 0.8 * hold_s)}
+
     def run(self, steps: int, warmup: int) -> dict:
         torch = self.torch
         for i in range(warmup):
@@ -164,6 +204,9 @@ class Bench:
         self.forward(0)
         kernel_ms = {nm: self._kernel_ms(k, steps) for k, nm in enumerate(STAGES) if nm in ("fc1", "fc2")}
         return dict(ms_step=ms_step, stage_ms=stage_ms, kernel_ms=kernel_ms)
+
+    def replay_stats(self) -> dict:
+        return self._replay_stats()
 
 
 def stored_traffic(workload: str):
@@ -192,6 +235,36 @@ def stored_traffic(workload: str):
             "write_scale": copy / (1024 * float(kv["copy_write_kib"]))}
 
 
+def stored_busy(workload: str):
+    """VALU / MFMA busy fractions of FC1 and FC2 from the stored counter runs, at the kernel durations
+    of a default bench run; None for a workload without a run, or when the GEMM sources changed."""
+    import hashlib
+    if not os.path.exists(BUSY_FILE):
+        return None
+    kv, sec = {}, None
+    for line in open(BUSY_FILE):
+        line = line.strip()
+        if line.startswith("["):
+            sec = line[1:line.index("]")]
+        elif "=" in line and not line.startswith("#"):
+            k, v = (x.strip() for x in line.split("=", 1))
+            kv[(sec, k) if sec and line != "" and k != "source_sha256" else k] = v
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "trellis_quantized_moe_tmoe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != kv.get("source_sha256"):
+        return None
+    out = {}
+    for fc in ("FC1", "FC2"):
+        sec = f"{workload} {fc}"
+        if (sec, "valu_busy_at_bench_time") in kv:
+            out[fc.lower()] = {"kernel": kv[(sec, "kernel")],
+                               "valu_busy": float(kv[(sec, "valu_busy_at_bench_time")]),
+                               "mfma_busy": float(kv[(sec, "mfma_busy_at_bench_time")])}
+    return out or None
+
+
 def cpu_baseline(inp, budget_s: float = 15.0):
     """The float64 oracle on host cores, repeated on the same workload for a bounded time."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -206,9 +279,26 @@ def cpu_baseline(inp, budget_s: float = 15.0):
         if time.perf_counter() - t0 >= budget_s or runs >= 20:
             break
     el = time.perf_counter() - t0
+    # one forward on a single thread, for the per-core figure
+    t1 = time.perf_counter()
+    oracle_np.forward(inp, mode="w4a8" if inp.name == "w4a8" else "w4a16", nthreads=1)
+    one = time.perf_counter() - t1
     return dict(value=inp.tokens * runs / el, unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"{runs} full forward(s) of the same workload ({inp.tokens} tokens each), "
-                       f"float64, {el:.1f} s"), y
+                       f"float64, {el:.1f} s",
+                one_thread_s_per_forward=one, one_thread_tokens_per_s=inp.tokens / one,
+                hardware_threads=int(oracle.load().orc_hardware_threads()), cpu_model=cpu_model()), y
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -254,6 +344,9 @@ def main():
         "kernel_ms": km,
         "fc2_gbs": fc2_gbs,
         "gemm_pair_gbs": (b.fc1_bytes + b.fc2_bytes) / ((km["fc1"] + km["fc2"]) * 1e-3) / 1e9,
+        "layer_weight_gbs": (b.fc1_bytes + b.fc2_bytes) / (ms * 1e-3) / 1e9,
+        "replay_us": b.replay_stats(),
+        "gemm_activity": stored_busy(args.workload),
     }
     y = b.y.cpu().numpy()
     if args.calibrate_copy:
@@ -284,7 +377,8 @@ def main():
             extra[f"{nm}:{t}"] = {"tokens_per_s": t / (rr["ms_step"] * 1e-3), "ms_per_step": rr["ms_step"],
                                   "gemm_tflops": tf, "gemm_tflops_frac": tf / peak, "gemm_weight_gbs": gbs,
                                   "gemm_weight_gbs_frac": gbs / HBM_PEAK_GBS, "stage_ms": s2, "kernel_ms": k2,
-                                  "touched_experts": e.touched, "weight_copies": e.n_copies}
+                                  "touched_experts": e.touched, "weight_copies": e.n_copies,
+                                  "gemm_activity": stored_busy(f"{nm}:{t}")}
             del e
             torch.cuda.empty_cache()
         out["extra"] = extra
