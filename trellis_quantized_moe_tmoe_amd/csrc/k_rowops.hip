@@ -223,9 +223,9 @@ struct CombineRotBody {
   }
 };
 
-// One workgroup of W wavefronts per token t, or (split_segments, few tokens with a long
-// non-power-of-two row) per (token, row segment): one 128-value block or the 64-value tail, as the
-// rotation never crosses a segment.
+// One workgroup of W wavefronts per token t (power-of-two rows, EPL > 0), or per (token, row segment)
+// for few tokens with a long non-power-of-two row (EPL = 0): one 128-value block or the 64-value
+// tail, as the rotation never crosses a segment (many tokens with such rows use k_combine_blocks).
 // Round it handles routes j = it * W + w (wavefront w): the split sum of v times scale2, rotated,
 // times sv2 and the route's weight, goes to the wavefront's LDS row (in registers up to 16 values
 // per lane; longer rows are staged in LDS and rotated there); after a barrier every thread adds its
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
   const int H = a.rot.n, K = a.top_k;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int t = blockIdx.x, seg = blockIdx.y;
-  const bool split = EPL == 0 && a.split_segments;
+  constexpr bool split = EPL == 0;
   const int off = split ? seg * 128 : 0;
   const int L = !split ? H : (seg < a.rot.nblk128 ? 128 : 64);
   float* acc = lds;                         // [L]
@@ -268,10 +268,10 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
 #pragma unroll
         for (int i = 0; i < S; ++i) row[64 * i + lane] = wt * (vv[i] * h2f(sg[64 * i]));
       };
-      if (split) {
+      if constexpr (split) {
         if (L == 128) in_registers(std::integral_constant<int, 2>{});
         else in_registers(std::integral_constant<int, 1>{});
-      } else if constexpr (EPL > 0 && EPL <= 16) {
+      } else if constexpr (EPL <= 16) {
         in_registers(std::integral_constant<int, EPL>{});
       } else {
         const float* src = a.v + static_cast<size_t>(p) * H + lane;
@@ -314,6 +314,71 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
     }
     __syncthreads();
   }
+}
+
+// Large batches with rows of a non-power-of-two length: one wavefront per (token t, rotation block),
+// which holds the block's S values per lane (S = 2: a 128-block; S = 1: the 64-value tail) through
+// all k routes: y_t[block] = sum over j ascending of w[t,j] * (sv2_e * R(scale2_e * v_slot[block])),
+// the same operations in the same order as the workgroup combine (no contraction into FMAs, so both
+// give the same bits). Lane j < k loads route j's slot, expert and weight once; routes are then taken
+// JB at a time with all of a batch's loads issued before the first is used. Dropped routes add
+// nothing. No LDS, no barrier.
+template <int S, int SMAX>
+__device__ __forceinline__ void combine_block(const CombineArgs& a, int t, int off, int lane) {
+#pragma clang fp contract(off)
+  constexpr int JB = 16 / SMAX;
+  const int H = a.rot.n, K = a.top_k;         // K <= 32
+  const size_t plane = static_cast<size_t>(a.routes) * H;
+  const int rl = t * K + (lane < K ? lane : K - 1);
+  const int p_l = lane < K ? a.route_slot[rl] : -1;
+  const int e_l = p_l >= 0 ? static_cast<int>(route_expert(a.ids, a.ids64, rl)) : 0;
+  const float w_l = p_l >= 0 ? a.w[rl] : 0.0f;
+  float acc[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) acc[i] = 0.0f;
+  for (int j0 = 0; j0 < K; j0 += JB) {
+    int p[JB];
+    float vv[JB][S], c2[JB][S], sg[JB][S];
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const int j = j0 + jb < K ? j0 + jb : K - 1;
+      p[jb] = j0 + jb < K ? __builtin_amdgcn_readlane(p_l, j) : -1;
+      const int e = __builtin_amdgcn_readlane(e_l, j);
+      const int pp = p[jb] >= 0 ? p[jb] : 0;
+      sum_splits<S, SMAX, SMAX>(a.v + static_cast<size_t>(pp) * H + off + lane, plane, SMAX, vv[jb]);
+      const uint16_t* cs = a.scale2 + static_cast<size_t>(e) * H + off + lane;
+      const uint16_t* ss = a.sv2 + static_cast<size_t>(e) * H + off + lane;
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        c2[jb][i] = h2f(cs[64 * i]);
+        sg[jb][i] = h2f(ss[64 * i]);
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      if (p[jb] < 0) continue;
+      const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), j0 + jb));
+#pragma unroll
+      for (int i = 0; i < S; ++i) vv[jb][i] *= c2[jb][i];
+      if (!a.rot.identity) fwht_segment<S>(vv[jb], lane);
+#pragma unroll
+      for (int i = 0; i < S; ++i) acc[i] += wt * (vv[jb][i] * sg[jb][i]);
+    }
+  }
+  float* out = a.y + static_cast<size_t>(t) * H + off + lane;
+#pragma unroll
+  for (int i = 0; i < S; ++i) out[64 * i] = acc[i];
+}
+
+template <int SMAX>
+__global__ __launch_bounds__(256) void k_combine_blocks(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int nseg = a.rot.nblk128 + a.rot.tail64;
+  const int item = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int t = item / nseg, seg = item - t * nseg;
+  if (t >= a.tokens) return;
+  if (seg < a.rot.nblk128) combine_block<2, SMAX>(a, t, seg * 128, lane);
+  else combine_block<1, SMAX>(a, t, seg * 128, lane);
 }
 
 struct DebugRotateBody {
@@ -401,7 +466,14 @@ void launch_act(const ActArgs& a, bool mx, hipStream_t s) {
 }
 
 void launch_combine(const CombineArgs& a, hipStream_t s) {
-  const bool split = !a.rot.pow2 && a.split_segments;
+  if (!a.rot.pow2 && !a.split_segments) {
+    const unsigned grid = blocks_for(static_cast<long long>(a.tokens) * row_segments(a.rot));
+    dispatch_smax(a.nsplit, [&](auto sm) {
+      hipLaunchKernelGGL((k_combine_blocks<decltype(sm)::value>), dim3(grid), dim3(256), 0, s, a);
+    });
+    return;
+  }
+  const bool split = !a.rot.pow2;                // few tokens: one workgroup per (token, segment)
   const int L = split ? 128 : a.rot.n;           // longest segment a workgroup combines
   const int W = combine_waves(L, a.top_k);
   const size_t lds = static_cast<size_t>(W + 1) * L * 4 + 4 * W;

@@ -347,6 +347,8 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   ca.sv2 = wt->sv2;
   ca.rot = make_rot(p->H, p->rotation == TMOE_ROT_IDENTITY);
   ca.y = y;
+  // non-power-of-two rows: few tokens (token x block items up to 2048) get a workgroup per (token,
+  // block) with one wavefront per route; more tokens a wavefront per (token, block) for all routes
   ca.split_segments = static_cast<long long>(T) * make_rot(p->H, 0).nblk128 <= 2048 ? 1 : 0;
   if (on(4)) launch_combine(ca, s);
 

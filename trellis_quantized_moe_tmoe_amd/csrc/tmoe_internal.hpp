@@ -87,7 +87,7 @@ struct CombineArgs {         // y_t = sum_j w[t,j] * sv2_e * R_H(scale2_e * v_sl
   const uint16_t* sv2;       // [E][H]
   RowRot rot;                // n = H
   float* y;                  // [T][H]
-  int split_segments;        // non-power-of-two H: one workgroup per (token, 128-block) instead of per token
+  int split_segments;        // non-power-of-two H: a workgroup (1) or a wavefront (0) per (token, block)
 };
 
 struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slot][k] * C_e[k][n]
