@@ -90,6 +90,33 @@ struct RotateBody {
     const uint16_t* sr = a.su1 + static_cast<size_t>(e) * H + off + lane;
 #pragma unroll
     for (int i = 0; i < S; ++i) v[i] = bf16_to_f32(xr[64 * i]) * h2f(sr[64 * i]);
+    finish<S>(v, off);
+  }
+  // NB consecutive 128-blocks from element off: every block's loads are issued before the first
+  // block is rotated (a long non-power-of-two row would otherwise wait on each block in turn).
+  template <int NB>
+  __device__ __forceinline__ void run_blocks128(int off) {
+    const uint16_t* xr = a.x + static_cast<size_t>(t) * H + off + lane;
+    const uint16_t* sr = a.su1 + static_cast<size_t>(e) * H + off + lane;
+    uint16_t xv[NB][2], sv[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        xv[nb][i] = xr[128 * nb + 64 * i];
+        sv[nb][i] = sr[128 * nb + 64 * i];
+      }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float v[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) v[i] = bf16_to_f32(xv[nb][i]) * h2f(sv[nb][i]);
+      finish<2>(v, off + 128 * nb);
+    }
+  }
+  // Rotation and store of one segment held strided (element off + 64 i + lane in v[i]).
+  template <int S>
+  __device__ __forceinline__ void finish(float (&v)[S], int off) {
     if (!a.rot.identity) fwht_segment<S>(v, lane);
     if constexpr (!MX) {
       _Float16* out = static_cast<_Float16*>(a.a1) + static_cast<size_t>(p) * a.lda + off + lane;
@@ -137,8 +164,16 @@ __device__ __forceinline__ void rotate_routes(const RotateArgs& a, int first) {
   const long long e = route_expert(a.ids, a.ids64, r);
   if (e < 0 || e >= a.num_experts) return;         // dropped route: its row is never read
   RotateBody<MX> body{a, lane, r, r / a.top_k, static_cast<int>(e), a.rot.n};
-  if (per > 1) run_segment<EPL>(a.rot, seg, body);
-  else for_segments<EPL>(a.rot, body);
+  if (per > 1) {
+    run_segment<EPL>(a.rot, seg, body);
+  } else if constexpr (EPL > 0) {
+    body.template run<EPL>(0);
+  } else {                          // the whole row: its 128-blocks four at a time, then the tail
+    int b = 0;
+    for (; b + 4 <= a.rot.nblk128; b += 4) body.template run_blocks128<4>(b * 128);
+    for (; b < a.rot.nblk128; ++b) body.template run_blocks128<1>(b * 128);
+    if (a.rot.tail64) body.template run<1>(a.rot.nblk128 * 128);
+  }
 }
 
 }  // namespace tmoe
