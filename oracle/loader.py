@@ -57,6 +57,8 @@ def _sig(lib):
     lib.orc_forward.restype = c.c_int
     lib.orc_route_trace.argtypes = ([c.c_int] * 5 + [P] * 10 + [c.c_int] * 4 + [P] * 6)
     lib.orc_route_trace.restype = c.c_int
+    lib.orc_linear.argtypes = [c.c_int] * 4 + [P] * 5 + [c.c_int, P]
+    lib.orc_linear.restype = c.c_int
     return lib
 
 

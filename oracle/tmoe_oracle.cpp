@@ -38,6 +38,11 @@
 //  R7 the W4A8 layer is the W4A16 layer with both rotated activations (FC1 and FC2 inputs)
 //     replaced by their MXFP8 quantize-dequantize, and each codebook value replaced by its
 //     E4M3 rounding (weight scale byte 127, i.e. 1.0); channel scales apply after the sum.
+//  R8 the dense trellis linear (sparkinfer PR #90 names a dense trellis GEMM and a trellis_linear
+//     API next to the fused MoE, with the same tiles, codebook and rotations, but prints no
+//     formula) is one trellis matrix C (K x N, R1-R3) between the layer's input rotation and its
+//     output rotation, with no routing and weight 1: y_t = sv * R_N(scale * (C^T R_K(su * x_t))),
+//     i.e. the FC1 input step, the FC2 contraction and scaling, and the combine's output step.
 #include <algorithm>
 #include <atomic>
 #include <cmath>
@@ -471,6 +476,34 @@ int orc_mxfp8_quantize(const double* in, int64_t rows, int cols, uint8_t* q, uin
       std::copy(in + r * cols + b * 32, in + r * cols + b * 32 + 32, tmp.begin());
       mx_qdq_block(tmp.data(), 32, q + r * cols + b * 32, e8m0 + r * (cols / 32) + b);
     }
+  }
+  return 0;
+}
+
+// Dense trellis linear (R8). payload: C's K/16 * N/16 tiles of 16*bits words; scale, sv: fp16 [N];
+// su: fp16 [K]; x: bf16 [T][K]; y: float64 [T][N]. Returns 0, or < 0 for an unsupported shape.
+int orc_linear(int T, int K, int N, int bits, const uint16_t* payload, const uint16_t* scale,
+               const uint16_t* su, const uint16_t* sv, const uint16_t* x, int identity, double* y) {
+  if (T < 0 || K <= 0 || N <= 0 || K % 16 || N % 16 || bits < 1 || bits > 16) return -1;
+  std::vector<std::pair<int, int>> blocks;
+  if (!hadamard_blocks(K, &blocks) || !hadamard_blocks(N, &blocks)) return -2;
+  std::vector<uint16_t> codes(static_cast<size_t>(K) * N);
+  decode_matrix(payload, bits, K, N, codes.data());
+  std::vector<double> c(codes.size());
+  for (size_t i = 0; i < codes.size(); ++i) c[i] = half_to_double(codes[i]);
+  std::vector<double> a(K), z(N);
+  for (int t = 0; t < T; ++t) {
+    for (int k = 0; k < K; ++k)
+      a[k] = half_to_double(su[k]) * bf16_to_double(x[static_cast<size_t>(t) * K + k]);
+    rotate(a.data(), K, identity != 0);
+    std::fill(z.begin(), z.end(), 0.0);
+    for (int k = 0; k < K; ++k) {
+      const double* row = c.data() + static_cast<size_t>(k) * N;
+      for (int n = 0; n < N; ++n) z[n] += a[k] * row[n];
+    }
+    for (int n = 0; n < N; ++n) z[n] *= half_to_double(scale[n]);
+    rotate(z.data(), N, identity != 0);
+    for (int n = 0; n < N; ++n) y[static_cast<size_t>(t) * N + n] = half_to_double(sv[n]) * z[n];
   }
   return 0;
 }

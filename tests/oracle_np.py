@@ -130,3 +130,15 @@ def route_trace(inp, t: int, j: int, mode: str = "w4a16", identity: bool = False
                                *[_p(out[k]) for k in ("a", "z", "h", "b", "v", "o")])
     assert rc == 0, rc
     return out
+
+
+def linear(inp, identity: bool = False) -> np.ndarray:
+    """The oracle's dense trellis linear (reading R8): y = sv * R_N(scale * (C^T R_K(su * x)))."""
+    y = np.zeros((inp.tokens, inp.out_features), np.float64)
+    arrs = [np.ascontiguousarray(inp.payload, np.uint16), np.ascontiguousarray(inp.scale).view(np.uint16),
+            np.ascontiguousarray(inp.su).view(np.uint16), np.ascontiguousarray(inp.sv).view(np.uint16),
+            np.ascontiguousarray(inp.x_bf16, np.uint16)]
+    rc = lib().orc_linear(inp.tokens, inp.in_features, inp.out_features, inp.bits, *[_p(a) for a in arrs],
+                          int(identity), _p(y))
+    assert rc == 0, rc
+    return y

@@ -182,3 +182,53 @@ def all_cases():
         for t in g["tokens"]:
             out.append((name, t))
     return out
+
+
+# Dense trellis linear (one matrix, no routing): the decode geometry's FC1 shape as a single
+# matrix (E = 1, k = 1), and the wide geometry's hidden size as the non-power-of-two case.
+LINEAR_GEOMETRIES = {
+    "linear":      dict(in_features=1024, out_features=1024, bits=4, tokens=(1, 16, 2048)),
+    "linear_wide": dict(in_features=2560, out_features=320, bits=3, tokens=(16,)),
+}
+
+
+@dataclasses.dataclass
+class LinearInputs:
+    name: str
+    seed: int
+    in_features: int          # K
+    out_features: int         # N
+    tokens: int
+    bits: int
+    payload: np.ndarray       # uint16 [K/16 * N/16 * 16 * bits]
+    scale: np.ndarray         # float16 [N]
+    su: np.ndarray            # float16 [K], +-1
+    sv: np.ndarray            # float16 [N], +-1
+    x_bf16: np.ndarray        # uint16 [T, K]
+
+
+def make_linear_inputs(name: str = "linear", tokens: Optional[int] = None, seed: Optional[int] = None,
+                       in_features: Optional[int] = None, out_features: Optional[int] = None,
+                       bits: Optional[int] = None, identity_signs: bool = False) -> LinearInputs:
+    """Draw one dense-linear input set. Draw order: payload words -> scale -> su, sv -> x.
+    seed defaults to 7000 + tokens."""
+    g = LINEAR_GEOMETRIES[name]
+    K = int(in_features or g["in_features"])
+    N = int(out_features or g["out_features"])
+    B = int(bits or g["bits"])
+    T = int(tokens if tokens is not None else g["tokens"][0])
+    if seed is None:
+        seed = 7000 + T
+    rng = np.random.Generator(np.random.PCG64(seed))
+    payload = rng.integers(0, 1 << 16, size=(K // 16) * (N // 16) * 16 * B, dtype=np.uint16)
+    scale = (rng.uniform(0.5, 1.5, size=N) / 16.0).astype(np.float16)
+
+    def signs(n):
+        s = np.where(rng.random(n) < 0.5, -1.0, 1.0).astype(np.float16)
+        return np.ones(n, np.float16) if identity_signs else s
+
+    su = signs(K)
+    sv = signs(N)
+    x_bf16 = bf16_bits_from_f32(rng.standard_normal((T, K)).astype(np.float32))
+    return LinearInputs(name=name, seed=int(seed), in_features=K, out_features=N, tokens=T, bits=B,
+                        payload=payload, scale=scale, su=su, sv=sv, x_bf16=x_bf16)
