@@ -235,6 +235,54 @@ def stored_traffic(workload: str):
             "write_scale": copy / (1024 * float(kv["copy_write_kib"]))}
 
 
+class LinearBench:
+    """Dense trellis linear: inputs, weight copies (cycled past 1 GB), plan and scratch."""
+
+    def __init__(self, name: str, T: int):
+        import torch
+        from trellis_quantized_moe_tmoe_amd import layer as L
+        from trellis_quantized_moe_tmoe_amd.workloads import make_linear_inputs
+        self.torch = torch
+        self.inp = make_linear_inputs(name, tokens=T)
+        self.plan = L.LinearPlan.for_inputs(self.inp)
+        base = L.LinearWeightsDev.from_inputs(self.inp)
+        per_copy = sum(getattr(base, f).numel() * getattr(base, f).element_size() for f in base.FIELDS)
+        self.n_copies = max(1, math.ceil(COPY_FOOTPRINT / per_copy))
+        self.copies = [base] + [base.clone() for _ in range(self.n_copies - 1)]
+        self.x = torch.from_numpy(self.inp.x_bf16.view(np.int16).copy()).cuda()
+        self.scratch = self.plan.alloc_scratch()
+        self.y = torch.empty((T, self.inp.out_features), dtype=torch.float32, device="cuda")
+        self.weight_bytes = self.inp.in_features * self.inp.out_features * self.inp.bits // 8
+        self.flops = 2.0 * T * self.inp.in_features * self.inp.out_features
+
+    def run(self, steps: int) -> float:
+        """ms per call: `steps` calls cycling the weight copies, captured in one graph."""
+        torch = self.torch
+        fn = lambda i: self.plan.forward(self.x, self.copies[i % self.n_copies], self.scratch, y=self.y)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(3):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                fn(i)
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / steps)
+        del g
+        return best
+
+
 def stored_busy(workload: str):
     """VALU / MFMA busy fractions of FC1 and FC2 from the stored counter runs, at the kernel durations
     of a default bench run; None for a workload without a run, or when the GEMM sources changed."""
@@ -380,6 +428,18 @@ def main():
                                   "touched_experts": e.touched, "weight_copies": e.n_copies,
                                   "gemm_activity": stored_busy(f"{nm}:{t}")}
             del e
+            torch.cuda.empty_cache()
+        for nm, t in (("linear", 16), ("linear_4k", 16), ("linear_4k", 2048)):
+            lb = LinearBench(nm, t)
+            ms = lb.run(max(10, args.steps))
+            extra[f"{nm}:{t}"] = {"tokens_per_s": t / (ms * 1e-3), "ms_per_call": ms,
+                                  "shape": [lb.inp.in_features, lb.inp.out_features, lb.inp.bits],
+                                  "weight_gbs": lb.weight_bytes / (ms * 1e-3) / 1e9,
+                                  "weight_gbs_frac": lb.weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                  "tflops": lb.flops / (ms * 1e-3) / 1e12,
+                                  "tflops_frac": lb.flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                                  "weight_copies": lb.n_copies}
+            del lb
             torch.cuda.empty_cache()
         out["extra"] = extra
     print(json.dumps(out), flush=True)

@@ -152,6 +152,43 @@ tmoe_status tmoe_forward_stages(tmoe_plan_t plan, int32_t w4a8, int32_t first, i
 
 const char *tmoe_status_str(tmoe_status s);
 
+/* ---- dense trellis linear: one trellis matrix, no routing ----
+ * y_t = sv * R_N(scale * (C^T R_K(su * x_t))),  C: K x N in the layer's tile format and codebook.
+ * Source: "integrate EXL3 Trellis into the fused W4A16 API" (sparkinfer PR #90) names a dense
+ * trellis GEMM and a trellis_linear API beside the fused MoE, with the same tiles, codebook and
+ * rotations; it prints no formula, so this is the layer's input rotation, one trellis contraction
+ * with per-output-channel scales, and the layer's output rotation, with no routing and weight 1.
+ * Runs the layer's kernels: one launch rotates x and writes the tables, then the grouped GEMM of a
+ * single expert, then the output rotation (the combine with k = 1). */
+typedef struct {
+  int32_t in_features;         /* K: multiple of 64, 64..4096 (same rules as H)                 */
+  int32_t out_features;        /* N: same rules                                                 */
+  int32_t bits;                /* 2, 3 or 4                                                     */
+  int32_t max_tokens;          /* capacity T_max >= 1                                           */
+  int32_t rotation;            /* TMOE_ROT_HADAMARD or TMOE_ROT_IDENTITY                         */
+} tmoe_linear_config;
+
+typedef struct tmoe_linear_plan_s *tmoe_linear_plan_t;   /* opaque, host-only, immutable */
+
+typedef struct {                 /* device pointers, read only */
+  const uint16_t *payload;       /* C: (K/16)*(N/16) tiles of 16*bits words; 16-byte aligned   */
+  const uint16_t *scale;         /* fp16 [N] output-channel scales                             */
+  const uint16_t *su;            /* fp16 [K] input signs                                       */
+  const uint16_t *sv;            /* fp16 [N] output signs                                      */
+} tmoe_linear_weights;
+
+/* Validate and plan (host only). scratch_bytes / payload_words may be NULL. Errors: INVALID_ARG,
+ * UNSUPPORTED. */
+tmoe_status tmoe_linear_plan(const tmoe_linear_config *cfg, tmoe_linear_plan_t *out,
+                             size_t *scratch_bytes, size_t *payload_words);
+tmoe_status tmoe_linear_plan_destroy(tmoe_linear_plan_t plan);
+
+/* x: bf16 [T][K] (16-byte aligned); y: fp32 [T][N] (16-byte aligned), fully overwritten. Scratch
+ * rules as for the layer. T = 0 launches nothing. Deterministic; safe to capture in a hipGraph. */
+tmoe_status tmoe_linear_w4a16(tmoe_linear_plan_t plan, const void *x_bf16, int32_t T,
+                              const tmoe_linear_weights *weights, float *y, void *scratch,
+                              size_t scratch_bytes, void *stream);
+
 /* ---- test hooks: expose single steps so their bit-exactness can be graded ---- */
 
 /* Decode expert `expert`'s FC1 (matrix 0, H x 2I) or FC2 (matrix 1, I x H) with the same device

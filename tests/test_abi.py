@@ -140,3 +140,49 @@ def test_route_map_and_debug_validation(N):
     assert (v.a1_pitch, v.b_pitch) == (1024, 512)
     assert N.lib.tmoe_status_str(3).decode().startswith("scratch")
     N.lib.tmoe_plan_destroy(h)
+
+
+def _linear_plan(N, **kw):
+    d = dict(in_features=1024, out_features=1024, bits=4, max_tokens=16, rotation=0)
+    d.update(kw)
+    c = N.LinearConfig(d["in_features"], d["out_features"], d["bits"], d["max_tokens"], d["rotation"])
+    h = ctypes.c_void_p()
+    sb, pw = ctypes.c_size_t(), ctypes.c_size_t()
+    st = N.lib.tmoe_linear_plan(ctypes.byref(c), ctypes.byref(h), ctypes.byref(sb), ctypes.byref(pw))
+    return st, h, sb.value, pw.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0), (dict(in_features=2560, out_features=320, bits=3), 0), (dict(in_features=1000), 2),
+    (dict(out_features=48), 2), (dict(out_features=8192), 2), (dict(bits=5), 2), (dict(bits=0), 1),
+    (dict(bits=17), 1), (dict(max_tokens=0), 1), (dict(rotation=2), 1), (dict(in_features=-64), 1),
+])
+def test_linear_plan_validation(N, kw, status):
+    st, h, sb, pw = _linear_plan(N, **kw)
+    assert st == status
+    if st == 0:
+        K = kw.get("in_features", 1024)
+        Nf = kw.get("out_features", 1024)
+        assert pw == (K // 16) * (Nf // 16) * 16 * kw.get("bits", 4)
+        assert sb > 0
+        assert N.lib.tmoe_linear_plan_destroy(h) == 0
+
+
+def test_linear_fails_closed_before_any_launch(N):
+    """Bad arguments return an error before any device pointer (all fake here) is touched."""
+    st, h, sb, _ = _linear_plan(N, max_tokens=16)
+    assert st == 0
+    fake = ctypes.c_void_p(0x1000)
+    w = N.LinearWeights(0x1000, 0x1000, 0x1000, 0x1000)
+    call = N.lib.tmoe_linear_w4a16
+    assert call(h, fake, 17, ctypes.byref(w), fake, fake, sb, None) == 4          # T > max_tokens
+    assert call(h, fake, -1, ctypes.byref(w), fake, fake, sb, None) == 1          # T < 0
+    assert call(h, fake, 4, ctypes.byref(w), fake, fake, sb - 1, None) == 3       # short arena
+    assert call(h, fake, 4, ctypes.byref(w), fake, ctypes.c_void_p(0x1008), sb, None) == 3   # misaligned arena
+    assert call(h, fake, 4, None, fake, fake, sb, None) == 1                      # no weights
+    assert call(h, ctypes.c_void_p(0x1002), 4, ctypes.byref(w), fake, fake, sb, None) == 5  # x misaligned
+    bad = N.LinearWeights(0x1000, 0x1001, 0x1000, 0x1000)
+    assert call(h, fake, 4, ctypes.byref(bad), fake, fake, sb, None) == 5         # odd fp16 pointer
+    assert call(h, fake, 0, ctypes.byref(w), fake, fake, sb, None) == 0           # T = 0: nothing
+    assert call(None, fake, 4, ctypes.byref(w), fake, fake, sb, None) == 1
+    assert N.lib.tmoe_linear_plan_destroy(h) == 0

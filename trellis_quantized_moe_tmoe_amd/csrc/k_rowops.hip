@@ -277,19 +277,14 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
         const float* src = a.v + static_cast<size_t>(p) * H + lane;
         const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + lane;
         constexpr int U = 8;
-        for (int base = 0; base < H; base += 64 * U) {
-          if (base + 64 * U <= H) {
-            float sum[U];
-            sum_splits<U, SMAX, splits_unroll<U, SMAX>(1)>(src + base, plane, splits, sum);
+        // (here EPL >= 32: the row is one block of 64 * EPL values, a multiple of 512); unrolled,
+        // so every chunk's loads can be in flight before the first LDS write
 #pragma unroll
-            for (int i = 0; i < U; ++i) row[base + 64 * i + lane] = sum[i] * h2f(c2[base + 64 * i]);
-          } else {
-            for (int c = base; c < H; c += 64) {
-              float one[1];
-              sum_splits<1, SMAX, SMAX>(src + c, plane, splits, one);
-              row[c + lane] = one[0] * h2f(c2[c]);
-            }
-          }
+        for (int base = 0; base < 64 * EPL; base += 64 * U) {
+          float sum[U];
+          sum_splits<U, SMAX, splits_unroll<U, SMAX>(1)>(src + base, plane, splits, sum);
+#pragma unroll
+          for (int i = 0; i < U; ++i) row[base + 64 * i + lane] = sum[i] * h2f(c2[base + 64 * i]);
         }
         CombineRotBody body{a, row, lane, e, a.w[r]};
         for_segments<EPL>(a.rot, body);
@@ -379,6 +374,31 @@ __global__ __launch_bounds__(256) void k_combine_blocks(CombineArgs a) {
   if (t >= a.tokens) return;
   if (seg < a.rot.nblk128) combine_block<2, SMAX>(a, t, seg * 128, lane);
   else combine_block<1, SMAX>(a, t, seg * 128, lane);
+}
+
+// Dense trellis linear, before its GEMM: workgroups [0, rot_blocks) rotate the tokens' rows, one
+// item per wavefront (a whole row, or one 128-block of a long non-power-of-two row while tokens are
+// few); the others write the GEMM tiles of the single expert and the combine's route tables.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_linear_prep(LinearPrepArgs a) {
+  if (static_cast<int>(blockIdx.x) < a.rot_blocks) {
+    const int per = EPL > 0 ? 1 : rotate_items_per_route(a.rot);
+    const int item = static_cast<int>(blockIdx.x * 4 + (threadIdx.x >> 6));
+    const int t = item / per, seg = item - t * per;
+    if (t < a.tokens) rotate_item<EPL, false>(a.rot, t, t, 0, seg, per);
+    return;
+  }
+  const int i0 = (static_cast<int>(blockIdx.x) - a.rot_blocks) * 256 + static_cast<int>(threadIdx.x);
+  const int stride = (static_cast<int>(gridDim.x) - a.rot_blocks) * 256;
+  for (int i = i0; i < a.tokens; i += stride) {
+    a.slot[i] = i;
+    a.ids[i] = 0;
+    a.w[i] = 1.0f;
+  }
+  const int nt = (a.tokens + a.tile_rows - 1) / a.tile_rows;
+  for (int i = i0; i < nt; i += stride)
+    a.gtiles[i] = make_int4(a.bits << 24, i * a.tile_rows, min(a.tile_rows, a.tokens - i * a.tile_rows), 0);
+  if (i0 == 0) *a.num_gtiles = nt;
 }
 
 struct DebugRotateBody {
@@ -483,6 +503,14 @@ void launch_combine(const CombineArgs& a, hipStream_t s) {
       constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;
       hipLaunchKernelGGL((k_combine<E, SM>), grid, dim3(64 * W), lds, s, a);
     });
+  });
+}
+
+void launch_linear_prep(const LinearPrepArgs& a, hipStream_t s) {
+  const int meta = std::max(1, std::min(64, (a.tokens + 255) / 256));
+  const dim3 grid(a.rot_blocks + meta);
+  dispatch_epl(a.rot.rot, [&](auto epl) {
+    hipLaunchKernelGGL((k_linear_prep<decltype(epl)::value>), grid, dim3(256), 0, s, a);
   });
 }
 

@@ -359,6 +359,118 @@ bool dim_ok(int n) { return n >= 64 && n <= kMaxDim && n % 64 == 0; }
 
 }  // namespace
 
+// ---------------------------------------------------------------- dense trellis linear
+// y_t = sv * R_N(scale * (C^T R_K(su * x_t))): the layer's input rotation, one trellis matrix (as
+// the grouped GEMM of a single expert whose tiles hold every token) and the layer's output
+// rotation with one route of weight 1 per token (the combine with k = 1).
+struct tmoe_linear_plan_s {
+  int K, N, bits, max_tokens, rotation;
+  int max_gtiles;
+  size_t gtiles, scalars, slot, ids, w, a1, z, total;    // arena offsets
+};
+
+namespace {
+
+// Tile rows of the dense GEMM: every weight is decoded once per tile, so the tile holds all tokens
+// up to 64 (16, 32 or 64 rows), and 128-row workgroup tiles beyond (when N allows them).
+int linear_mg(int T, int N) {
+  if (T <= 16) return 1;
+  if (T <= 32) return 2;
+  if (T <= 64) return 4;
+  if (N % 256 == 0) return 16;
+  if (N % 128 == 0) return 8;
+  return 4;
+}
+
+tmoe_status linear_forward(const tmoe_linear_plan_s* p, const void* x, int32_t T, const tmoe_linear_weights* wt,
+                           float* y, void* scratch, size_t bytes, hipStream_t s) {
+  if (T < 0) return TMOE_ERR_INVALID_ARG;
+  if (T > p->max_tokens) return TMOE_ERR_CAPACITY;
+  if (!scratch || !aligned(scratch, 16) || bytes < p->total) return TMOE_ERR_SCRATCH;
+  if (T == 0) return TMOE_OK;
+  if (!x || !wt || !y || !wt->payload || !wt->scale || !wt->su || !wt->sv) return TMOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(wt->payload, 16) || !aligned(wt->scale, 2) ||
+      !aligned(wt->su, 2) || !aligned(wt->sv, 2))
+    return TMOE_ERR_ALIGNMENT;
+
+  const int mg = linear_mg(T, p->N);
+  const int rows = tile_rows(mg);
+  const bool big = mg >= 8;
+  const int ntiles = (T + rows - 1) / rows;
+  const int ng = p->N / (mg == 16 ? 256 : big ? 128 : 64);
+  const int splits = choose_splits(T, p->K / 32);
+  long long waves = std::min<long long>(big ? kGemmGroupCap : kGemmWaveCap, 1LL * ntiles * ng * splits);
+  if (big) {                                    // a whole number of 8-tile rounds of units
+    const long long per = 8LL * ng * splits;
+    waves = (waves + per - 1) / per * per;
+  }
+
+  LinearPrepArgs lp;
+  lp.rot.x = static_cast<const uint16_t*>(x);
+  lp.rot.ids = nullptr;
+  lp.rot.ids64 = 0;
+  lp.rot.top_k = 1;
+  lp.rot.num_experts = 1;
+  lp.rot.su1 = wt->su;
+  lp.rot.rot = make_rot(p->K, p->rotation == TMOE_ROT_IDENTITY);
+  lp.rot.a1 = at<uint8_t>(scratch, p->a1);
+  lp.rot.a1_scale = nullptr;
+  lp.rot.lda = fp16_pitch(p->K);
+  lp.rot.routes = T;
+  lp.rot.split_segments = T < 2048 ? 1 : 0;
+  lp.gtiles = at<int4>(scratch, p->gtiles);
+  lp.num_gtiles = at<int32_t>(scratch, p->scalars);
+  lp.slot = at<int32_t>(scratch, p->slot);
+  lp.ids = at<int32_t>(scratch, p->ids);
+  lp.w = at<float>(scratch, p->w);
+  lp.tokens = T;
+  lp.tile_rows = rows;
+  lp.bits = p->bits;
+  const RowRot& rk = lp.rot.rot;
+  const long long items = 1LL * T * (rk.pow2 || !lp.rot.split_segments ? 1 : rk.nblk128 + rk.tail64);
+  lp.rot_blocks = static_cast<int>((items + 3) / 4);
+
+  GemmArgs g;
+  g.payload = wt->payload;
+  g.einfo = nullptr;
+  g.fc2_words_per_bit = 0;
+  g.a = lp.rot.a1;
+  g.arow = nullptr;
+  g.a_scale = nullptr;
+  g.out = at<float>(scratch, p->z);
+  g.gtiles = lp.gtiles;
+  g.num_gtiles = lp.num_gtiles;
+  g.nsplit = splits;
+  g.K = p->K;
+  g.N = p->N;
+  g.lda = lp.rot.lda;
+  g.routes = T;
+
+  CombineArgs ca;
+  ca.v = g.out;
+  ca.nsplit = splits;
+  ca.ids = lp.ids;
+  ca.ids64 = 0;
+  ca.w = lp.w;
+  ca.route_slot = lp.slot;
+  ca.top_k = 1;
+  ca.tokens = T;
+  ca.routes = T;
+  ca.scale2 = wt->scale;
+  ca.sv2 = wt->sv;
+  ca.rot = make_rot(p->N, p->rotation == TMOE_ROT_IDENTITY);
+  ca.y = y;
+  ca.split_segments = static_cast<long long>(T) * make_rot(p->N, 0).nblk128 <= 2048 ? 1 : 0;
+
+  (void)hipGetLastError();
+  launch_linear_prep(lp, s);
+  launch_gemm_f16(g, 1, p->bits, mg, static_cast<int>(waves), s);
+  launch_combine(ca, s);
+  return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 tmoe_status tmoe_plan(const tmoe_config* cfg, tmoe_plan_t* out, size_t* scratch_bytes, size_t* payload_words) {
@@ -529,6 +641,53 @@ tmoe_status tmoe_debug_get_views(tmoe_plan_t p, int32_t T, int32_t w4a8, void* s
   out->a1_pitch = w4a8 ? p->H : fp16_pitch(p->H);
   out->b_pitch = w4a8 ? p->I : fp16_pitch(p->I);
   return TMOE_OK;
+}
+
+tmoe_status tmoe_linear_plan(const tmoe_linear_config* cfg, tmoe_linear_plan_t* out, size_t* scratch_bytes,
+                             size_t* payload_words) {
+  if (!cfg || !out) return TMOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (cfg->in_features <= 0 || cfg->out_features <= 0 || cfg->max_tokens <= 0 || cfg->bits <= 0 || cfg->bits > 16)
+    return TMOE_ERR_INVALID_ARG;
+  if (cfg->rotation != TMOE_ROT_HADAMARD && cfg->rotation != TMOE_ROT_IDENTITY) return TMOE_ERR_INVALID_ARG;
+  if (!dim_ok(cfg->in_features) || !dim_ok(cfg->out_features)) return TMOE_ERR_UNSUPPORTED;
+  if (cfg->bits < 2 || cfg->bits > 4) return TMOE_ERR_UNSUPPORTED;
+  if (cfg->max_tokens > kMaxRoutes) return TMOE_ERR_UNSUPPORTED;
+  tmoe_linear_plan_s* p = new (std::nothrow) tmoe_linear_plan_s();
+  if (!p) return TMOE_ERR_INVALID_ARG;
+  p->K = cfg->in_features;
+  p->N = cfg->out_features;
+  p->bits = cfg->bits;
+  p->max_tokens = cfg->max_tokens;
+  p->rotation = cfg->rotation;
+  const long long T = cfg->max_tokens;
+  p->max_gtiles = static_cast<int>(T / 16 + 1);
+  size_t off = 0;
+  auto take = [&](size_t b) { size_t o = off; off = align_up(off + b); return o; };
+  p->gtiles = take(16ull * p->max_gtiles);
+  p->scalars = take(32);
+  p->slot = take(4ull * T);
+  p->ids = take(4ull * T);
+  p->w = take(4ull * T);
+  p->a1 = take(2ull * T * fp16_pitch(p->K));
+  const int ks = p->K / 32;
+  p->z = take(4ull * max_split_rows(T, ks, ks) * p->N);
+  p->total = off;
+  *out = p;
+  if (scratch_bytes) *scratch_bytes = p->total;
+  if (payload_words) *payload_words = static_cast<size_t>(p->K / 16) * (p->N / 16) * 16 * p->bits;
+  return TMOE_OK;
+}
+
+tmoe_status tmoe_linear_plan_destroy(tmoe_linear_plan_t plan) {
+  delete plan;
+  return TMOE_OK;
+}
+
+tmoe_status tmoe_linear_w4a16(tmoe_linear_plan_t p, const void* x, int32_t T, const tmoe_linear_weights* w,
+                              float* y, void* scratch, size_t bytes, void* stream) {
+  if (!p) return TMOE_ERR_INVALID_ARG;
+  return linear_forward(p, x, T, w, y, scratch, bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -106,6 +106,18 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
   int routes;                // R: row stride between split planes
 };
 
+struct LinearPrepArgs {      // dense trellis linear: a = R_K(su * x_t) per token, plus the tables the
+                             // grouped GEMM and the combine read (one expert, one route per token)
+  RotateArgs rot;            // x, su1 = su, rot (n = K), a1, lda, routes = T; ids unused
+  int4* gtiles;              // ceil(T / tile_rows) tiles of expert 0
+  int32_t* num_gtiles;
+  int32_t* slot;             // [T] t
+  int32_t* ids;              // [T] 0
+  float* w;                  // [T] 1
+  int tokens, tile_rows, bits;
+  int rot_blocks;            // workgroups of rotation items; the rest write the tables
+};
+
 // one workgroup for up to kRouteSingleMax routes, else a counting and a placement launch over
 // workgroups of kRouteChunk routes each
 constexpr int kRouteChunk = 1024;
@@ -113,6 +125,7 @@ constexpr int kRouteSingleMax = 4096;
 // the route map and, in the same launch (extra workgroups, independent work), the input rotation
 void launch_route_map(const RouteMapArgs& a, const RotateArgs* rot, bool mx, hipStream_t s);
 void launch_act(const ActArgs& a, bool mx, hipStream_t s);
+void launch_linear_prep(const LinearPrepArgs& a, hipStream_t s);
 void launch_combine(const CombineArgs& a, hipStream_t s);
 // fc: 1 or 2 (names the kernel); bits: the width shared by every expert (2, 3, 4) or 0 if mixed;
 // mg: 16-row groups per GEMM tile (1, 2 or 4); waves: persistent wave count

@@ -152,18 +152,12 @@ __host__ __device__ inline int rotate_items_per_route(const RotateArgs& a) {
   return a.split_segments ? row_segments(a.rot) : 1;
 }
 
-// Workgroup-level input rotation, one item per wavefront: item first + wave. Used by the route-map
-// launch for its extra workgroups (the rotation does not depend on the route map).
+// One rotation item of operand row p (token t's x with expert e's signs): segment seg of the row
+// when rows are split into `per` items, else the whole row.
 template <int EPL, bool MX>
-__device__ __forceinline__ void rotate_routes(const RotateArgs& a, int first) {
+__device__ __forceinline__ void rotate_item(const RotateArgs& a, int p, int t, int e, int seg, int per) {
   const int lane = threadIdx.x & 63;
-  const int per = EPL > 0 ? 1 : rotate_items_per_route(a);
-  const int item = first + static_cast<int>(threadIdx.x >> 6);
-  const int r = item / per, seg = item - r * per;
-  if (r >= a.routes) return;
-  const long long e = route_expert(a.ids, a.ids64, r);
-  if (e < 0 || e >= a.num_experts) return;         // dropped route: its row is never read
-  RotateBody<MX> body{a, lane, r, r / a.top_k, static_cast<int>(e), a.rot.n};
+  RotateBody<MX> body{a, lane, p, t, e, a.rot.n};
   if (per > 1) {
     run_segment<EPL>(a.rot, seg, body);
   } else if constexpr (EPL > 0) {
@@ -174,6 +168,19 @@ __device__ __forceinline__ void rotate_routes(const RotateArgs& a, int first) {
     for (; b < a.rot.nblk128; ++b) body.template run_blocks128<1>(b * 128);
     if (a.rot.tail64) body.template run<1>(a.rot.nblk128 * 128);
   }
+}
+
+// Workgroup-level input rotation, one item per wavefront: item first + wave. Used by the route-map
+// launch for its extra workgroups (the rotation does not depend on the route map).
+template <int EPL, bool MX>
+__device__ __forceinline__ void rotate_routes(const RotateArgs& a, int first) {
+  const int per = EPL > 0 ? 1 : rotate_items_per_route(a);
+  const int item = first + static_cast<int>(threadIdx.x >> 6);
+  const int r = item / per, seg = item - r * per;
+  if (r >= a.routes) return;
+  const long long e = route_expert(a.ids, a.ids64, r);
+  if (e < 0 || e >= a.num_experts) return;         // dropped route: its row is never read
+  rotate_item<EPL, MX>(a, r, r / a.top_k, static_cast<int>(e), seg, per);
 }
 
 }  // namespace tmoe

@@ -170,3 +170,74 @@ def scratch_view(scratch: torch.Tensor, ptr: int, shape, dtype) -> torch.Tensor:
     if off < 0 or off + n > scratch.numel():
         raise ValueError("pointer outside the scratch arena")
     return scratch[off:off + n].view(dtype).view(shape)
+
+
+class LinearWeightsDev:
+    """Device copies of one dense trellis matrix: payload words, fp16 output scales and sign vectors."""
+
+    FIELDS = ("payload", "scale", "su", "sv")
+
+    def __init__(self, payload: torch.Tensor, scale, su, sv):
+        self.payload, self.scale, self.su, self.sv = payload, scale, su, sv
+        self._c = native.LinearWeights(*[t.data_ptr() for t in (payload, scale, su, sv)])
+
+    @classmethod
+    def from_inputs(cls, inp, device="cuda") -> "LinearWeightsDev":
+        def up(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+        return cls(up(inp.payload, np.int16), *[up(getattr(inp, n), np.float16) for n in ("scale", "su", "sv")])
+
+    def clone(self) -> "LinearWeightsDev":
+        return LinearWeightsDev(*[getattr(self, n).clone() for n in self.FIELDS])
+
+    @property
+    def c(self) -> native.LinearWeights:
+        return self._c
+
+
+class LinearPlan:
+    """Dense trellis linear y = sv * R_N(scale * (C^T R_K(su * x))) (include/tmoe.h)."""
+
+    def __init__(self, in_features: int, out_features: int, bits: int, max_tokens: int, rotation: str = "hadamard"):
+        self.config = native.LinearConfig(in_features, out_features, bits, max_tokens,
+                                          native.ROT_IDENTITY if rotation == "identity" else native.ROT_HADAMARD)
+        handle = ctypes.c_void_p()
+        sb, pw = ctypes.c_size_t(), ctypes.c_size_t()
+        check(lib.tmoe_linear_plan(ctypes.byref(self.config), ctypes.byref(handle), ctypes.byref(sb),
+                                   ctypes.byref(pw)), "tmoe_linear_plan")
+        self.handle = handle
+        self.scratch_bytes = sb.value
+        self.payload_words = pw.value
+        self.in_features, self.out_features, self.max_tokens = in_features, out_features, max_tokens
+
+    @classmethod
+    def for_inputs(cls, inp, max_tokens: Optional[int] = None, **kw) -> "LinearPlan":
+        return cls(inp.in_features, inp.out_features, inp.bits, max_tokens or max(inp.tokens, 1), **kw)
+
+    def close(self):
+        if getattr(self, "handle", None) and self.handle.value:
+            lib.tmoe_linear_plan_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc_scratch(self, device="cuda") -> torch.Tensor:
+        return torch.empty(self.scratch_bytes, dtype=torch.uint8, device=device)
+
+    def forward(self, x: torch.Tensor, weights: LinearWeightsDev, scratch: torch.Tensor,
+                y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.out_features), dtype=torch.float32, device=x.device)
+        check(lib.tmoe_linear_w4a16(self.handle, _ptr(x), T, ctypes.byref(weights.c), _ptr(y), _ptr(scratch),
+                                    scratch.numel(), _stream(x.device)), "tmoe_linear_w4a16")
+        return y
+
+    def forward_status(self, x, T, weights, y, scratch, scratch_bytes, stream=None) -> int:
+        """Raw status of a call with explicit (possibly invalid) arguments; for tests."""
+        wc = ctypes.byref(weights.c) if isinstance(weights, LinearWeightsDev) else weights
+        return lib.tmoe_linear_w4a16(self.handle, x, T, wc, y, scratch, scratch_bytes, stream)

@@ -20,7 +20,8 @@ IDS_I32, IDS_I64 = 0, 1
 EXPORTS = ["tmoe_plan", "tmoe_plan_destroy", "tmoe_plan_get_info", "tmoe_plan_expert_offset",
            "tmoe_build_route_map", "tmoe_forward_w4a16", "tmoe_forward_w4a8", "tmoe_forward_stages",
            "tmoe_status_str",
-           "tmoe_debug_decode", "tmoe_debug_mxfp8", "tmoe_debug_rotate", "tmoe_debug_get_views"]
+           "tmoe_debug_decode", "tmoe_debug_mxfp8", "tmoe_debug_rotate", "tmoe_debug_get_views",
+           "tmoe_linear_plan", "tmoe_linear_plan_destroy", "tmoe_linear_w4a16"]
 
 
 class Config(ctypes.Structure):
@@ -49,6 +50,15 @@ class PlanInfo(ctypes.Structure):
 class DebugViews(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("a1", "a1_scale", "z", "b", "b_scale", "v", "splits")] + \
                [("a1_pitch", ctypes.c_int32), ("b_pitch", ctypes.c_int32)]
+
+
+class LinearConfig(ctypes.Structure):
+    _fields_ = [("in_features", ctypes.c_int32), ("out_features", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("rotation", ctypes.c_int32)]
+
+
+class LinearWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("payload", "scale", "su", "sv")]
 
 
 class TmoeError(RuntimeError):
@@ -84,6 +94,10 @@ def _load():
     lib.tmoe_debug_mxfp8.argtypes = [P, I64, I32, P, P, P]
     lib.tmoe_debug_rotate.argtypes = [P, I64, I32, P]
     lib.tmoe_debug_get_views.argtypes = [P, I32, I32, P, SZ, ctypes.POINTER(DebugViews)]
+    lib.tmoe_linear_plan.argtypes = [ctypes.POINTER(LinearConfig), ctypes.POINTER(P), ctypes.POINTER(SZ),
+                                     ctypes.POINTER(SZ)]
+    lib.tmoe_linear_plan_destroy.argtypes = [P]
+    lib.tmoe_linear_w4a16.argtypes = [P, P, I32, ctypes.POINTER(LinearWeights), P, P, SZ, P]
     for name in EXPORTS:
         if name != "tmoe_status_str":
             getattr(lib, name).restype = I32

@@ -185,10 +185,12 @@ def all_cases():
 
 
 # Dense trellis linear (one matrix, no routing): the decode geometry's FC1 shape as a single
-# matrix (E = 1, k = 1), and the wide geometry's hidden size as the non-power-of-two case.
+# matrix (E = 1, k = 1), the wide geometry's hidden size as the non-power-of-two case, and the
+# largest supported square matrix (8 MB of 4-bit payload) for measurement.
 LINEAR_GEOMETRIES = {
     "linear":      dict(in_features=1024, out_features=1024, bits=4, tokens=(1, 16, 2048)),
     "linear_wide": dict(in_features=2560, out_features=320, bits=3, tokens=(16,)),
+    "linear_4k":   dict(in_features=4096, out_features=4096, bits=4, tokens=(16, 2048)),
 }
 
 
