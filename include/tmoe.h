@@ -70,7 +70,7 @@ typedef struct {
   int32_t num_experts;         /* E: 1..512                                                   */
   int32_t top_k;               /* k: 1..32                                                    */
   int32_t max_tokens;          /* capacity T_max >= 1; T*k <= 2^24                            */
-  const uint8_t *expert_bits;  /* host array [E], each 2, 3 or 4; copied by tmoe_plan          */
+  const uint8_t *expert_bits;  /* host array [E], each 2..6 (W4A8: 2..4); copied by tmoe_plan  */
   int32_t rotation;            /* TMOE_ROT_HADAMARD or TMOE_ROT_IDENTITY                       */
   int32_t ids_dtype;           /* TMOE_IDS_I32 or TMOE_IDS_I64                                 */
   int32_t block_m;             /* route-map tile rows: 8, 16, 32, 48 or 64; 0 = 16             */
@@ -163,7 +163,7 @@ const char *tmoe_status_str(tmoe_status s);
 typedef struct {
   int32_t in_features;         /* K: multiple of 64, 64..4096 (same rules as H)                 */
   int32_t out_features;        /* N: same rules                                                 */
-  int32_t bits;                /* 2, 3 or 4                                                     */
+  int32_t bits;                /* 2..6                                                          */
   int32_t max_tokens;          /* capacity T_max >= 1                                           */
   int32_t rotation;            /* TMOE_ROT_HADAMARD or TMOE_ROT_IDENTITY                         */
 } tmoe_linear_config;

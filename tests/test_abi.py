@@ -64,7 +64,8 @@ def test_plan_validation(N, kw, status):
         assert N.lib.tmoe_plan_destroy(h) == 0
 
 
-@pytest.mark.parametrize("bits,status", [([4, 3, 2], 0), ([4, 5], 2), ([1], 2), ([0], 1), ([17], 1)])
+@pytest.mark.parametrize("bits,status", [([4, 3, 2], 0), ([4, 5], 0), ([6, 5, 2], 0), ([7], 2), ([1], 2),
+                                         ([0], 1), ([17], 1)])
 def test_plan_bit_widths(N, bits, status):
     assert _plan(N, bits)[0] == status
 
@@ -154,7 +155,8 @@ def _linear_plan(N, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(), 0), (dict(in_features=2560, out_features=320, bits=3), 0), (dict(in_features=1000), 2),
-    (dict(out_features=48), 2), (dict(out_features=8192), 2), (dict(bits=5), 2), (dict(bits=0), 1),
+    (dict(out_features=48), 2), (dict(out_features=8192), 2), (dict(bits=5), 0), (dict(bits=6), 0),
+    (dict(bits=7), 2), (dict(bits=0), 1),
     (dict(bits=17), 1), (dict(max_tokens=0), 1), (dict(rotation=2), 1), (dict(in_features=-64), 1),
 ])
 def test_linear_plan_validation(N, kw, status):
@@ -186,3 +188,14 @@ def test_linear_fails_closed_before_any_launch(N):
     assert call(h, fake, 0, ctypes.byref(w), fake, fake, sb, None) == 0           # T = 0: nothing
     assert call(None, fake, 4, ctypes.byref(w), fake, fake, sb, None) == 1
     assert N.lib.tmoe_linear_plan_destroy(h) == 0
+
+
+def test_w4a8_rejects_widths_above_four(N):
+    """The fp8 path decodes widths 2-4; a plan holding a 5- or 6-bit expert runs W4A16 only."""
+    st, h, sb, _ = _plan(N, [4, 5, 4, 6])
+    assert st == 0
+    fake = 1 << 20
+    w = N.Weights(*([fake] * 7))
+    args = [h, fake, fake, fake, 4, ctypes.byref(w), fake, fake, sb, None]
+    assert N.lib.tmoe_forward_w4a8(*args) == 2
+    N.lib.tmoe_plan_destroy(h)

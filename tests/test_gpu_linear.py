@@ -47,6 +47,8 @@ class LinearCase:
     ("linear", 2048, {}),                                          # full size of the prefill-like case
     ("linear", 16, dict(bits=2)),
     ("linear", 16, dict(bits=3)),
+    ("linear", 16, dict(bits=5)),                                  # two half windows per 8-element group
+    ("linear", 300, dict(bits=6, in_features=512, out_features=256)),  # 64-row tiles at widths 5-6
     ("linear_wide", 16, {}),                                       # 2560 x 320, 3-bit, both rotations blocked
     ("linear_wide", 2100, dict(in_features=320, out_features=2560)),   # many tokens: per-route rotation,
                                                                    # per-block combine wavefronts

@@ -78,6 +78,35 @@ def test_decode_bit_exact(name, T, experts):
             assert np.array_equal(got8, lut[want]), (e, m, "e4m3")
 
 
+@pytest.mark.parametrize("bits", [5, 6])
+def test_decode_bit_exact_widths_5_6(bits):
+    """Widths 5 and 6 read each 8-element group as two half windows (its states span up to 58 bits)."""
+    c = Case("tiny", 4, bits_override=bits)
+    lut = e4m3_of_fp16_table()
+    for e in range(c.inp.experts):
+        c1, c2 = O.expert_codes(c.inp, e)
+        for m, want in ((0, c1), (1, c2)):
+            got = c.plan.debug_decode(c.weights, e, m).cpu().numpy().view(np.uint16)
+            assert np.array_equal(got, want), (e, m)
+            got8 = c.plan.debug_decode(c.weights, e, m, as_e4m3=True).cpu().numpy()
+            assert np.array_equal(got8, lut[want]), (e, m)
+
+
+@pytest.mark.parametrize("name,T,over", [
+    ("tiny", 4, dict(bits_override=5)),                          # 16-row tiles
+    ("tiny", 4, dict(bits_override=6)),
+    ("decode", 16, dict(bits_override=6)),
+    ("tiny", 300, dict(bits_override=5)),                        # 64-row tiles (no 128-row tiles at 5-6)
+    ("tiny", 40, dict(bits_choices=(2, 3, 4, 5, 6))),            # mixed 2-6, 64-row tiles
+    ("wide", 16, dict(bits_choices=(2, 3, 4, 5, 6), hidden=640, inter=320, experts=16)),
+])
+def test_layer_w4a16_widths_5_6(name, T, over):
+    c = Case(name, T, **over)
+    err = rel_err(c.run().cpu().numpy(), c.oracle_w4a16)
+    say(f"[result] {c.label} bits {sorted(set(c.inp.bits.tolist()))} rel err {err:.3e}")
+    assert err <= TOL_W4A16
+
+
 def test_mxfp8_quantizer_bit_exact():
     from trellis_quantized_moe_tmoe_amd.layer import debug_mxfp8
     rng = np.random.default_rng(11)

@@ -170,7 +170,7 @@ template <bool COOP>
 __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4* scan_smem, TableSmem& tb) {
   const int tid = threadIdx.x, E = a.num_experts;
   const bool own = tid < E;                      // E <= 512 < 1024: one expert per thread
-  const int bits_e = own ? static_cast<int>((a.packed_bits[tid >> 4] >> (2 * (tid & 15))) & 3u) + 2 : 0;
+  const int bits_e = own ? static_cast<int>((a.packed_bits[tid >> 3] >> (4 * (tid & 7))) & 15u) : 0;
   const int tiles_e = own ? (total_e + a.block_m - 1) / a.block_m : 0;
   const int gtiles_e = own ? (total_e + a.gemm_rows - 1) / a.gemm_rows : 0;
   int4 totals;

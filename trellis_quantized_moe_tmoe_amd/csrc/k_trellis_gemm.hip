@@ -166,7 +166,87 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
     }
 }
 
-// BITS = 0: experts of mixed widths, chosen per unit. FC (1 or 2) only names the instantiation,
+// One wavefront unit of the fp16 GEMM for widths 5 and 6. A lane reads the two half windows of its
+// 8-element group per strip (four words, tmoe_device.hpp) and its A fragment straight into
+// registers, one K step ahead of the step it decodes; the compiler places the waits. Same unit,
+// lane mapping and output as unit_f16.
+template <int BITS, int MG>
+__device__ __forceinline__ void unit_f16_wide(const GemmArgs& a, const int4 t, int ng, int s, int splits, int lane,
+                                              uint32_t mask, uint32_t orv) {
+  constexpr int TW = 8 * BITS;                         // 32-bit words per 16x16 tile
+  constexpr int NW = TW;
+  const long long woff = (static_cast<long long>(static_cast<unsigned>(t.w)) << 8);
+  const int row0 = t.y, rows = t.z;
+  const int NT = a.N >> 4;
+  const int col = lane & 15, grp = lane >> 4;
+  const int q = 2 * col + (grp & 1);
+  const int ksteps = (a.K >> 5) / splits;
+  const int ks0 = s * ksteps, ks1 = ks0 + ksteps;
+  const int nt0 = ng * NS;
+  const uint32_t* mat = reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS) +
+                        static_cast<size_t>(nt0) * TW + static_cast<size_t>(grp >> 1) * NT * TW;
+  const size_t kstride = static_cast<size_t>(2) * NT * TW;    // words between K steps (two tile rows)
+  const int j0 = half_window_word<BITS>(2 * q), j1 = half_window_word<BITS>(2 * q + 1);
+  const int r0 = j0 < 0 ? j0 + NW : j0, r1 = j0 + 1 == NW ? 0 : j0 + 1;
+  const int r2 = j1 < 0 ? j1 + NW : j1, r3 = j1 + 1 == NW ? 0 : j1 + 1;
+  const _Float16* A = static_cast<const _Float16*>(a.a);
+  long long aoff[MG];
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg) aoff[mg] = operand_row(a, row0 + min(16 * mg + col, rows - 1)) * a.lda + 8 * grp;
+  f4 acc[MG][NS];
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) acc[mg][ns] = f4{0.f, 0.f, 0.f, 0.f};
+  uint32_t w[NS][4];
+  half8 aa[MG];
+  auto load = [&](int ks, uint32_t (&wd)[NS][4], half8 (&ad)[MG]) {
+    const uint32_t* base = mat + static_cast<size_t>(ks) * kstride;
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const uint32_t* tl = base + ns * TW;
+      wd[ns][0] = tl[r0];
+      wd[ns][1] = tl[r1];
+      wd[ns][2] = tl[r2];
+      wd[ns][3] = tl[r3];
+    }
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) ad[mg] = *reinterpret_cast<const half8*>(A + aoff[mg] + 32 * ks);
+  };
+  load(ks0, w, aa);
+  for (int ks = ks0; ks < ks1; ++ks) {
+    uint32_t wn[NS][4];
+    half8 an[MG];
+    load(ks + 1 < ks1 ? ks + 1 : ks, wn, an);          // the next step's operands (the last reloads its own)
+    half8 b[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) b[ns] = decode8_wide<BITS>(w[ns], q, mask, orv);
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+        acc[mg][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aa[mg], b[ns], acc[mg][ns], 0, 0, 0);
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[ns][k] = wn[ns][k];
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) aa[mg] = an[mg];
+  }
+  float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mg + 4 * grp + i;
+      if (r < rows) {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) o[static_cast<size_t>(r) * a.N + 16 * ns] = acc[mg][ns][i];
+      }
+    }
+}
+
+// BITS = 0: experts of mixed widths 2-4, chosen per unit; BITS = kMixedWide: mixed widths 2-6. FC (1 or 2) only names the instantiation,
 // so profiles tell the two GEMMs apart.
 template <int BITS, int MG, int FC>
 __device__ __forceinline__ void gemm_f16_body(const GemmArgs& a, uint32_t* ring_all) {
@@ -185,13 +265,19 @@ __device__ __forceinline__ void gemm_f16_body(const GemmArgs& a, uint32_t* ring_
     const int rest = u / splits;
     const int ng = rest % NG;
     const int4 t = a.gtiles[rest / NG];
-    if constexpr (BITS != 0) {
+    if constexpr (BITS == 5 || BITS == 6) {
+      unit_f16_wide<BITS, MG>(a, t, ng, s, splits, lane, mask, orv);
+    } else if constexpr (BITS != 0 && BITS != kMixedWide) {
       unit_f16<BITS, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
     } else {
       const int bits = (t.x >> 24) & 0xff;
       if (bits == 4) unit_f16<4, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
       else if (bits == 3) unit_f16<3, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
-      else unit_f16<2, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
+      else if (BITS == 0 || bits == 2) unit_f16<2, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
+      else if constexpr (BITS == kMixedWide) {
+        if (bits == 5) unit_f16_wide<5, MG>(a, t, ng, s, splits, lane, mask, orv);
+        else unit_f16_wide<6, MG>(a, t, ng, s, splits, lane, mask, orv);
+      }
     }
   }
 }
@@ -199,7 +285,7 @@ __device__ __forceinline__ void gemm_f16_body(const GemmArgs& a, uint32_t* ring_
 // Decode-size tiles (16 rows): sized to keep five wavefronts per SIMD resident, so a round of
 // units covers the chip evenly.
 template <int BITS, int MG, int FC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 0 ? 3 : 5, 8))) void k_gemm_f16_small(GemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 0 || BITS >= 5 ? 3 : 5, 8))) void k_gemm_f16_small(GemmArgs a) {
   __shared__ uint32_t ring_all[4 * ring_words<MG>()];
   gemm_f16_body<BITS, MG, FC>(a, ring_all);
 }
@@ -537,10 +623,17 @@ __global__ __launch_bounds__(256) void k_debug_decode(const uint16_t* words, int
   const int kt = 2 * kp + (grp >> 1);
   const uint32_t* tile = reinterpret_cast<const uint32_t*>(words) + static_cast<size_t>(kt * NT + nt) * TW;
   const uint32_t mask = vreg_const(kMcgMask);
-  uint32_t hi, lo;
-  load_window<BITS>(tile, q, hi, lo);
   uint32_t p[4];
-  decode8_pairs<BITS>(hi, lo, q, mask, kMcgOr, p);
+  if constexpr (BITS >= 5) {
+    uint32_t w[4];
+    load_window_half<BITS>(tile, 2 * q, w[0], w[1]);
+    load_window_half<BITS>(tile, 2 * q + 1, w[2], w[3]);
+    decode8_pairs_wide<BITS>(w[0], w[1], w[2], w[3], q, mask, kMcgOr, p);
+  } else {
+    uint32_t hi, lo;
+    load_window<BITS>(tile, q, hi, lo);
+    decode8_pairs<BITS>(hi, lo, q, mask, kMcgOr, p);
+  }
   const int k0 = 16 * kt + 8 * (grp & 1);
   const int n = 16 * nt + col;
   if (!as_e4m3) {
@@ -575,12 +668,24 @@ void launch_f8(const GemmArgs& a, int mg, dim3 grid, hipStream_t s) {
   else hipLaunchKernelGGL((k_gemm_f8<BITS, 1, FC>), grid, dim3(256), 0, s, a);
 }
 
+// Widths 5 and 6 (uniform, or in a mixed set) run only the per-wavefront kernels (tiles of up to
+// 64 rows); the host never asks for 128-row tiles then.
+template <int BITS, int FC>
+void launch_f16_narrow(const GemmArgs& a, int mg, dim3 grid, hipStream_t s) {
+  if (mg >= 4) hipLaunchKernelGGL((k_gemm_f16<BITS, 4, FC>), grid, dim3(256), 0, s, a);
+  else if (mg == 2) hipLaunchKernelGGL((k_gemm_f16<BITS, 2, FC>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_gemm_f16_small<BITS, 1, FC>), grid, dim3(256), 0, s, a);
+}
+
 template <int FC>
 void launch_f16_bits(const GemmArgs& a, int bits, int mg, dim3 grid, hipStream_t s) {
   switch (bits) {
     case 4: launch_f16<4, FC>(a, mg, grid, s); break;
     case 3: launch_f16<3, FC>(a, mg, grid, s); break;
     case 2: launch_f16<2, FC>(a, mg, grid, s); break;
+    case 5: launch_f16_narrow<5, FC>(a, mg, grid, s); break;
+    case 6: launch_f16_narrow<6, FC>(a, mg, grid, s); break;
+    case kMixedWide: launch_f16_narrow<kMixedWide, FC>(a, mg, grid, s); break;
     default: launch_f16<0, FC>(a, mg, grid, s); break;
   }
 }
@@ -615,6 +720,8 @@ void launch_debug_decode(const uint16_t* matrix_words, int bits, int K, int N, i
   const dim3 grid((units + 3) / 4), block(256);
   if (bits == 4) hipLaunchKernelGGL(k_debug_decode<4>, grid, block, 0, s, matrix_words, K, N, as_e4m3, out);
   else if (bits == 3) hipLaunchKernelGGL(k_debug_decode<3>, grid, block, 0, s, matrix_words, K, N, as_e4m3, out);
+  else if (bits == 5) hipLaunchKernelGGL(k_debug_decode<5>, grid, block, 0, s, matrix_words, K, N, as_e4m3, out);
+  else if (bits == 6) hipLaunchKernelGGL(k_debug_decode<6>, grid, block, 0, s, matrix_words, K, N, as_e4m3, out);
   else hipLaunchKernelGGL(k_debug_decode<2>, grid, block, 0, s, matrix_words, K, N, as_e4m3, out);
 }
 

@@ -157,6 +157,59 @@ __device__ __forceinline__ half8 decode8(uint32_t hi_raw, uint32_t lo_raw, int q
   return __builtin_bit_cast(half8, v);
 }
 
+// Widths 5 and 6. The states of eight consecutive elements span up to 7*BITS + 16 = 58 stream bits,
+// which one window of two 32-bit words does not hold at every offset, so a group of eight is read
+// as two halves of four (elements 8q..8q+3 = half 2q, 8q+4..8q+7 = half 2q+1). A half's states span
+// 3*BITS + 16 bits starting at most 30 bits into the word holding its first bit (the start offsets
+// 20h - 11 and 24h - 10 modulo 32 never exceed 29 and 30), so the two words from there hold it.
+template <int BITS>
+__device__ __forceinline__ int half_window_word(int h) {
+  return ((4 * h + 1) * BITS - 16) >> 5;            // floor: negative for h = 0 (the stream wraps)
+}
+
+// Raw words (j0, j0 + 1) of half h's window in a tile of 8*BITS words, indices modulo the tile.
+template <int BITS>
+__device__ __forceinline__ void load_window_half(const uint32_t* __restrict__ tile, int h, uint32_t& hi,
+                                                 uint32_t& lo) {
+  constexpr int NW = 8 * BITS;
+  const int j0 = half_window_word<BITS>(h);
+  hi = tile[j0 < 0 ? j0 + NW : j0];
+  lo = tile[j0 + 1 == NW ? 0 : j0 + 1];
+}
+
+// State of element 4h+jj from its half's window, both words as big-endian strings (x first).
+template <int BITS>
+__device__ __forceinline__ uint32_t half_state(uint32_t x, uint32_t l, int h, int jj) {
+  const int shift = 64 - ((4 * h + jj + 1) * BITS - 32 * half_window_word<BITS>(h));   // 0..48
+  const uint32_t v = shift >= 32 ? (x >> (shift - 32)) : __builtin_amdgcn_alignbit(x, l, shift);
+  return v & 0xffffu;
+}
+
+// Elements 8q .. 8q+7 (widths 5, 6) from the raw windows of halves 2q (h0) and 2q+1 (h1), as four
+// packed fp16 pairs (element 8q+2i in the low half of p[i]).
+template <int BITS>
+__device__ __forceinline__ void decode8_pairs_wide(uint32_t h0_hi, uint32_t h0_lo, uint32_t h1_hi, uint32_t h1_lo,
+                                                   int q, uint32_t mask, uint32_t orv, uint32_t (&p)[4]) {
+  const uint32_t x0 = be32(h0_hi), l0 = be32(h0_lo), x1 = be32(h1_hi), l1 = be32(h1_lo);
+  uint32_t m[8];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    m[jj] = mcg_bits(half_state<BITS>(x0, l0, 2 * q, jj), mask, orv);
+    m[4 + jj] = mcg_bits(half_state<BITS>(x1, l1, 2 * q + 1, jj), mask, orv);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = code_pair(m[2 * i], m[2 * i + 1]);
+}
+
+template <int BITS>
+__device__ __forceinline__ half8 decode8_wide(const uint32_t (&w)[4], int q, uint32_t mask, uint32_t orv) {
+  uint32_t p[4];
+  decode8_pairs_wide<BITS>(w[0], w[1], w[2], w[3], q, mask, orv, p);
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  const u4v v = {p[0], p[1], p[2], p[3]};
+  return __builtin_bit_cast(half8, v);
+}
+
 // The mask and OR constants live in registers for v_and_or_b32 (no 32-bit literal in VOP3 here);
 // loading them through an opaque move keeps them from being folded back into two instructions.
 __device__ __forceinline__ uint32_t vreg_const(uint32_t c) {

@@ -84,11 +84,12 @@ struct tmoe_plan_s {
   int H, I, E, K, max_tokens, rotation, ids64, block_m;
   std::vector<uint8_t> bits;
   std::vector<long long> offsets;   // word offset per expert, [E+1]
-  uint32_t packed_bits[32];
+  uint32_t packed_bits[64];      // 4 bits per expert: its width
   long long routes_max;
   int max_tiles, max_gtiles;
   bool fp8_ok;
-  int uniform_bits;                 // the width shared by all experts, or 0 if they differ
+  int uniform_bits;                 // the width shared by all experts; 0 (mixed 2-4) or kMixedWide
+  int max_bits;
   Layout lay;
 };
 
@@ -182,7 +183,7 @@ GemmShape gemm_shape(const tmoe_plan_s* p, long long R, int mg, bool fp8, int fc
 }
 
 int big_cols(const tmoe_plan_s* p, bool fp8) {
-  if (fp8) return 0;
+  if (fp8 || p->max_bits > 4) return 0;      // 128-row tiles: widths 2-4 only
   for (int c : {256, 128})
     if (p->H % c == 0 && (2 * p->I) % c == 0) return c;
   return 0;
@@ -393,7 +394,7 @@ tmoe_status linear_forward(const tmoe_linear_plan_s* p, const void* x, int32_t T
       !aligned(wt->su, 2) || !aligned(wt->sv, 2))
     return TMOE_ERR_ALIGNMENT;
 
-  const int mg = linear_mg(T, p->N);
+  const int mg = p->bits > 4 ? std::min(linear_mg(T, p->N), 4) : linear_mg(T, p->N);   // 128-row tiles: widths 2-4
   const int rows = tile_rows(mg);
   const bool big = mg >= 8;
   const int ntiles = (T + rows - 1) / rows;
@@ -490,7 +491,7 @@ tmoe_status tmoe_plan(const tmoe_config* cfg, tmoe_plan_t* out, size_t* scratch_
   for (int e = 0; e < cfg->num_experts; ++e) {
     const int b = cfg->expert_bits[e];
     if (b < 1 || b > 16) return TMOE_ERR_INVALID_ARG;
-    if (b < 2 || b > 4) return TMOE_ERR_UNSUPPORTED;
+    if (b < 2 || b > 6) return TMOE_ERR_UNSUPPORTED;
   }
   tmoe_plan_s* p = new (std::nothrow) tmoe_plan_s();
   if (!p) return TMOE_ERR_INVALID_ARG;
@@ -507,15 +508,17 @@ tmoe_status tmoe_plan(const tmoe_config* cfg, tmoe_plan_t* out, size_t* scratch_
   std::memset(p->packed_bits, 0, sizeof(p->packed_bits));
   for (int e = 0; e < p->E; ++e) {
     p->offsets[e + 1] = p->offsets[e] + 3LL * p->H * p->I * p->bits[e] / 16;
-    p->packed_bits[e >> 4] |= static_cast<uint32_t>(p->bits[e] - 2) << (2 * (e & 15));
+    p->packed_bits[e >> 3] |= static_cast<uint32_t>(p->bits[e]) << (4 * (e & 7));
   }
   p->routes_max = rmax;
   p->max_tiles = static_cast<int>(rmax / p->block_m + p->E + 1);
   p->max_gtiles = static_cast<int>(rmax / 16 + p->E + 1);
-  p->fp8_ok = (p->H % 128 == 0) && (p->I % 128 == 0);
+  // W4A8 decodes widths 2-4 only (its kernel reads one two-word window per group of eight)
+  p->max_bits = *std::max_element(p->bits.begin(), p->bits.end());
+  p->fp8_ok = (p->H % 128 == 0) && (p->I % 128 == 0) && p->max_bits <= 4;
   p->uniform_bits = p->bits[0];
   for (int e = 1; e < p->E; ++e)
-    if (p->bits[e] != p->bits[0]) p->uniform_bits = 0;
+    if (p->bits[e] != p->bits[0]) p->uniform_bits = p->max_bits <= 4 ? 0 : kMixedWide;
   build_layout(p);
   *out = p;
   if (scratch_bytes) *scratch_bytes = p->lay.total;
@@ -651,7 +654,7 @@ tmoe_status tmoe_linear_plan(const tmoe_linear_config* cfg, tmoe_linear_plan_t* 
     return TMOE_ERR_INVALID_ARG;
   if (cfg->rotation != TMOE_ROT_HADAMARD && cfg->rotation != TMOE_ROT_IDENTITY) return TMOE_ERR_INVALID_ARG;
   if (!dim_ok(cfg->in_features) || !dim_ok(cfg->out_features)) return TMOE_ERR_UNSUPPORTED;
-  if (cfg->bits < 2 || cfg->bits > 4) return TMOE_ERR_UNSUPPORTED;
+  if (cfg->bits < 2 || cfg->bits > 6) return TMOE_ERR_UNSUPPORTED;
   if (cfg->max_tokens > kMaxRoutes) return TMOE_ERR_UNSUPPORTED;
   tmoe_linear_plan_s* p = new (std::nothrow) tmoe_linear_plan_s();
   if (!p) return TMOE_ERR_INVALID_ARG;

@@ -31,7 +31,7 @@ struct RouteMapArgs {
   int32_t* slot_expert;     // [R]: expert of each slot, -1 past the filled slots
   int32_t* wg_counts;       // [workgroups][E + 1]: per-workgroup counts (large batches; E = invalid)
   ExpertInfo* einfo;
-  uint32_t packed_bits[32]; // 2 bits per expert: bits - 2
+  uint32_t packed_bits[64]; // 4 bits per expert: its width
 };
 
 // Rotation of a row of n values: one power-of-two block (pow2 = true, EPL = n / 64 values per
@@ -117,6 +117,9 @@ struct LinearPrepArgs {      // dense trellis linear: a = R_K(su * x_t) per toke
   int tokens, tile_rows, bits;
   int rot_blocks;            // workgroups of rotation items; the rest write the tables
 };
+
+// GEMM width code for experts of mixed widths that include 5 or 6 (0: mixed widths 2-4)
+constexpr int kMixedWide = 7;
 
 // one workgroup for up to kRouteSingleMax routes, else a counting and a placement launch over
 // workgroups of kRouteChunk routes each

@@ -119,12 +119,14 @@ def _zipf_ids(rng: np.random.Generator, tokens: int, experts: int, k: int, s: fl
 def make_inputs(name: str, tokens: Optional[int] = None, seed: Optional[int] = None,
                 identity_signs: bool = False, bits_override: Optional[int] = None,
                 hidden: Optional[int] = None, inter: Optional[int] = None,
-                experts: Optional[int] = None, top_k: Optional[int] = None) -> LayerInputs:
+                experts: Optional[int] = None, top_k: Optional[int] = None,
+                bits_choices: Optional[tuple] = None) -> LayerInputs:
     """Draw one input set for geometry `name` (see GEOMETRIES).
 
     seed defaults to 1000*geometry_index + tokens. identity_signs sets every sign vector to +1
     (used with the identity-rotation test mode). Shape overrides make small variants of a
-    geometry for edge-case tests; the draw order is unchanged."""
+    geometry for edge-case tests; bits_override (one width) or bits_choices (widths drawn per
+    expert) replace the geometry's widths. The draw order is unchanged."""
     g = GEOMETRIES[name]
     H = int(hidden or g["hidden"])
     I = int(inter or g["inter"])
@@ -136,6 +138,8 @@ def make_inputs(name: str, tokens: Optional[int] = None, seed: Optional[int] = N
     rng = np.random.Generator(np.random.PCG64(seed))
 
     choices = g["bits"] if bits_override is None else (bits_override,)
+    if bits_choices is not None:
+        choices = tuple(bits_choices)
     if len(choices) > 1:
         bits = rng.choice(np.asarray(choices, dtype=np.uint8), size=E)
     else:
