@@ -99,6 +99,8 @@ def test_decode_bit_exact_widths_5_6(bits):
     ("tiny", 300, dict(bits_override=5)),                        # 64-row tiles (no 128-row tiles at 5-6)
     ("tiny", 40, dict(bits_choices=(2, 3, 4, 5, 6))),            # mixed 2-6, 64-row tiles
     ("wide", 16, dict(bits_choices=(2, 3, 4, 5, 6), hidden=640, inter=320, experts=16)),
+    ("tiny", 64, dict(bits_choices=(2, 3, 4, 5, 6), experts=512, top_k=8)),   # the most experts: all 64
+                                                                 # words of packed widths (4 bits each)
 ])
 def test_layer_w4a16_widths_5_6(name, T, over):
     c = Case(name, T, **over)
