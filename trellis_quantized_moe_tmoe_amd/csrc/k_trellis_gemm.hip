@@ -11,8 +11,8 @@
 // Units are dealt to a persistent grid whose size is fixed on the host, so the launch is
 // graph-capturable although the tile count is only known on the device. Within a unit the payload
 // words and activation fragments of the next steps are kept in flight in an LDS ring filled by
-// direct global->LDS loads (the fp16 kernels) or in registers (the fp8 kernel), so the decode of
-// one step overlaps the memory latency of the next ones.
+// direct global->LDS loads (the fp16 kernels, widths 2-4) or in registers (the fp8 kernel, and the
+// fp16 unit for widths 5 and 6), so the decode of one step overlaps the memory latency of the next.
 //
 // Operand layouts (gfx950, checked on hardware):
 //  * v_mfma_f32_16x16x32_f16: A lane l = row l%16, k = 8*(l/16)+[0,8); B lane l = column l%16,

@@ -23,7 +23,7 @@ typedef short s2v __attribute__((ext_vector_type(2)));
 
 struct ExpertInfo {          // written into scratch by the route-map kernel
   long long word_offset;     // first 16-bit word of the expert's region (FC1 then FC2)
-  int bits;                  // 2, 3 or 4
+  int bits;                  // 2..6
   int pad;
 };
 
