@@ -11,8 +11,8 @@
 // Units are dealt to a persistent grid whose size is fixed on the host, so the launch is
 // graph-capturable although the tile count is only known on the device. Within a unit the payload
 // words and activation fragments of the next steps are kept in flight in an LDS ring filled by
-// direct global->LDS loads (the fp16 kernels, widths 2-4) or in registers (the fp8 kernel, and the
-// fp16 unit for widths 5 and 6), so the decode of one step overlaps the memory latency of the next.
+// direct global->LDS loads (the fp16 kernels) or in registers (the fp8 kernel), so the decode of
+// one step overlaps the memory latency of the next ones.
 //
 // Operand layouts (gfx950, checked on hardware):
 //  * v_mfma_f32_16x16x32_f16: A lane l = row l%16, k = 8*(l/16)+[0,8); B lane l = column l%16,
@@ -48,13 +48,18 @@ __device__ __forceinline__ gptr<T> uniform_ptr(const T* p) {
 // One wavefront unit of the fp16 GEMM. Every K step's operands arrive with direct global->LDS
 // loads (16 bytes per lane) into the wavefront's own slot of an LDS ring DF steps deep: the step's
 // trellis words (two 16-deep tile rows x NS strips = 2*NS*TW 32-bit words, 1 KB at 4 bits; lane L
-// copies chunk L) and its A fragments (MG x 1 KB; each lane copies exactly the 16 bytes it later
+// copies chunk L, and at widths 5 and 6 lanes L < 16 or 32 also chunk 64 + L) and its A fragments (MG x 1 KB; each lane copies exactly the 16 bytes it later
 // feeds to the MFMA). The memory pipeline thus holds DF steps per wavefront without registers, and
 // the only waits are on the ring. Rows of the A fragment beyond the tile are not loaded (first row
 // group) or repeat the tile's last row (later groups); their output rows are never stored (an MFMA
 // output row depends on its own A row only), so no masking sits in the MFMA chain.
-template <int MG>
-constexpr int ring_words() { return DF * (2 * NS * 32 + MG * 256); }
+// Ring words of one wavefront for a kernel instantiated at width code BITS: its slots hold 2*NS
+// tiles of up to 4 bits (widths 2-4, and BITS = 0 for mixed 2-4) or of the width itself (5, 6; 6
+// for kMixedWide), then the A fragments.
+template <int BITS>
+constexpr int ring_tile_bits() { return BITS == kMixedWide ? 6 : (BITS > 4 ? BITS : 4); }
+template <int BITS, int MG>
+constexpr int ring_words() { return DF * (2 * NS * 8 * ring_tile_bits<BITS>() + MG * 256); }
 
 // Operand row of slot p: the FC1 input is stored per route (arow maps slot -> route), the FC2 input
 // per slot.
@@ -67,8 +72,11 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
                                          uint32_t* ring, uint32_t mask, uint32_t orv) {
   constexpr int TW = 8 * BITS;                         // 32-bit words per 16x16 tile
   constexpr int BW = 2 * NS * TW;                      // trellis words per K step
-  constexpr int STAGE = 2 * NS * 32 + MG * 256;        // words per ring slot (sized for 4 bits)
+  constexpr int AOFF = 2 * NS * 8 * ring_tile_bits<BITS>();   // A fragments follow the trellis words
+  constexpr int STAGE = AOFF + MG * 256;               // words per ring slot
   constexpr int CPT = TW / 4;                          // 16-byte chunks per tile
+  constexpr int NL = BW / 4 > 64 ? 2 : 1;              // staging loads per step (5 and 6 bits: 80, 96 chunks)
+  static_assert(BW / 4 <= 128, "two staging loads per step at most");
   const long long woff = (static_cast<long long>(static_cast<unsigned>(t.w)) << 8);
   const int row0 = t.y, rows = t.z;
   const int NT = a.N >> 4;
@@ -84,11 +92,19 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
   const bool stager = lane < BW / 4;
   const int st_tile = lane / (NS * CPT), st_strip = (lane / CPT) % NS, st_chunk = lane % CPT;
   const int st_off = (st_tile * NT + st_strip) * TW + 4 * st_chunk;          // words, relative to the step
+  // widths 5 and 6: lane L < BW/4 - 64 also copies chunk 64 + L, to ring word 256 + 4L
+  const int c2 = 64 + lane;
+  const bool stager2 = NL == 2 && c2 < BW / 4;
+  const int st2_off = ((c2 / (NS * CPT)) * NT + (c2 / CPT) % NS) * TW + 4 * (c2 % CPT);
   const int kstride = 2 * NT * TW;                                            // words between K steps
-  // reading: window words of group q in tile row (grp>>1) of strip ns
-  const int j0 = window_word<BITS>(q);
+  // reading: window words of group q in tile row (grp>>1) of strip ns (widths 5, 6: the two half
+  // windows of the group, tmoe_device.hpp)
+  const int j0 = BITS >= 5 ? half_window_word<BITS>(2 * q) : window_word<BITS>(q);
   const int rd_a = (grp >> 1) * NS * TW + (j0 < 0 ? j0 + TW : j0);
   const int rd_b = (grp >> 1) * NS * TW + ((j0 + 1 == TW) ? 0 : j0 + 1);
+  const int j1 = BITS >= 5 ? half_window_word<BITS>(2 * q + 1) : 0;
+  const int rd_c = (grp >> 1) * NS * TW + (j1 < 0 ? j1 + TW : j1);
+  const int rd_d = (grp >> 1) * NS * TW + ((j1 + 1 == TW) ? 0 : j1 + 1);
   long long aoff[MG];
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg) aoff[mg] = operand_row(a, row0 + min(16 * mg + col, rows - 1)) * a.lda + 8 * grp;
@@ -109,29 +125,45 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
     if (stager)
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(mat + static_cast<size_t>(ks) * kstride + st_off),
                                        (void __attribute__((address_space(3)))*)(slot), 16, 0, 0);
+    if constexpr (NL == 2) {
+      if (stager2)
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(mat + static_cast<size_t>(ks) * kstride + st2_off),
+                                         (void __attribute__((address_space(3)))*)(slot + 256), 16, 0, 0);
+    }
     const gptr<_Float16> ab = A + 32 * ks;
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg)
       if (mg > 0 || a_live)
         __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(ab + aoff[mg]),
-                                         (void __attribute__((address_space(3)))*)(slot + 2 * NS * 32 + mg * 256), 16, 0, 0);
+                                         (void __attribute__((address_space(3)))*)(slot + AOFF + mg * 256), 16, 0, 0);
   };
   auto step = [&](int d, int next) {
     // the direct loads of the DF-1 younger steps may still be in flight
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DF - 1) * (1 + MG)) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DF - 1) * (NL + MG)) : "memory");
     const uint32_t* slot = ring + d * STAGE;
-    uint32_t wh[NS], wl[NS];
+    uint32_t wh[NS], wl[NS], wc[NS], wd[NS];           // wc, wd: second half windows (widths 5, 6)
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
       wh[ns] = slot[rd_a + ns * TW];
       wl[ns] = slot[rd_b + ns * TW];
+      if constexpr (BITS >= 5) {
+        wc[ns] = slot[rd_c + ns * TW];
+        wd[ns] = slot[rd_d + ns * TW];
+      }
     }
     half8 aa[MG];
 #pragma unroll
-    for (int mg = 0; mg < MG; ++mg) aa[mg] = *reinterpret_cast<const half8*>(slot + 2 * NS * 32 + mg * 256 + 4 * lane);
+    for (int mg = 0; mg < MG; ++mg) aa[mg] = *reinterpret_cast<const half8*>(slot + AOFF + mg * 256 + 4 * lane);
     half8 b[NS];
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) b[ns] = decode8<BITS>(wh[ns], wl[ns], q, mask, orv);
+    for (int ns = 0; ns < NS; ++ns) {
+      if constexpr (BITS >= 5) {
+        const uint32_t w4[4] = {wh[ns], wl[ns], wc[ns], wd[ns]};
+        b[ns] = decode8_wide<BITS>(w4, q, mask, orv);
+      } else {
+        b[ns] = decode8<BITS>(wh[ns], wl[ns], q, mask, orv);
+      }
+    }
     // every LDS read of this slot has returned before the slot is refilled
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     issue(next, d);
@@ -166,86 +198,6 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
     }
 }
 
-// One wavefront unit of the fp16 GEMM for widths 5 and 6. A lane reads the two half windows of its
-// 8-element group per strip (four words, tmoe_device.hpp) and its A fragment straight into
-// registers, one K step ahead of the step it decodes; the compiler places the waits. Same unit,
-// lane mapping and output as unit_f16.
-template <int BITS, int MG>
-__device__ __forceinline__ void unit_f16_wide(const GemmArgs& a, const int4 t, int ng, int s, int splits, int lane,
-                                              uint32_t mask, uint32_t orv) {
-  constexpr int TW = 8 * BITS;                         // 32-bit words per 16x16 tile
-  constexpr int NW = TW;
-  const long long woff = (static_cast<long long>(static_cast<unsigned>(t.w)) << 8);
-  const int row0 = t.y, rows = t.z;
-  const int NT = a.N >> 4;
-  const int col = lane & 15, grp = lane >> 4;
-  const int q = 2 * col + (grp & 1);
-  const int ksteps = (a.K >> 5) / splits;
-  const int ks0 = s * ksteps, ks1 = ks0 + ksteps;
-  const int nt0 = ng * NS;
-  const uint32_t* mat = reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS) +
-                        static_cast<size_t>(nt0) * TW + static_cast<size_t>(grp >> 1) * NT * TW;
-  const size_t kstride = static_cast<size_t>(2) * NT * TW;    // words between K steps (two tile rows)
-  const int j0 = half_window_word<BITS>(2 * q), j1 = half_window_word<BITS>(2 * q + 1);
-  const int r0 = j0 < 0 ? j0 + NW : j0, r1 = j0 + 1 == NW ? 0 : j0 + 1;
-  const int r2 = j1 < 0 ? j1 + NW : j1, r3 = j1 + 1 == NW ? 0 : j1 + 1;
-  const _Float16* A = static_cast<const _Float16*>(a.a);
-  long long aoff[MG];
-#pragma unroll
-  for (int mg = 0; mg < MG; ++mg) aoff[mg] = operand_row(a, row0 + min(16 * mg + col, rows - 1)) * a.lda + 8 * grp;
-  f4 acc[MG][NS];
-#pragma unroll
-  for (int mg = 0; mg < MG; ++mg)
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) acc[mg][ns] = f4{0.f, 0.f, 0.f, 0.f};
-  uint32_t w[NS][4];
-  half8 aa[MG];
-  auto load = [&](int ks, uint32_t (&wd)[NS][4], half8 (&ad)[MG]) {
-    const uint32_t* base = mat + static_cast<size_t>(ks) * kstride;
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      const uint32_t* tl = base + ns * TW;
-      wd[ns][0] = tl[r0];
-      wd[ns][1] = tl[r1];
-      wd[ns][2] = tl[r2];
-      wd[ns][3] = tl[r3];
-    }
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg) ad[mg] = *reinterpret_cast<const half8*>(A + aoff[mg] + 32 * ks);
-  };
-  load(ks0, w, aa);
-  for (int ks = ks0; ks < ks1; ++ks) {
-    uint32_t wn[NS][4];
-    half8 an[MG];
-    load(ks + 1 < ks1 ? ks + 1 : ks, wn, an);          // the next step's operands (the last reloads its own)
-    half8 b[NS];
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) b[ns] = decode8_wide<BITS>(w[ns], q, mask, orv);
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg)
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-        acc[mg][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aa[mg], b[ns], acc[mg][ns], 0, 0, 0);
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) w[ns][k] = wn[ns][k];
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg) aa[mg] = an[mg];
-  }
-  float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
-#pragma unroll
-  for (int mg = 0; mg < MG; ++mg)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mg + 4 * grp + i;
-      if (r < rows) {
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) o[static_cast<size_t>(r) * a.N + 16 * ns] = acc[mg][ns][i];
-      }
-    }
-}
-
 // BITS = 0: experts of mixed widths 2-4, chosen per unit; BITS = kMixedWide: mixed widths 2-6. FC (1 or 2) only names the instantiation,
 // so profiles tell the two GEMMs apart.
 template <int BITS, int MG, int FC>
@@ -258,16 +210,14 @@ __device__ __forceinline__ void gemm_f16_body(const GemmArgs& a, uint32_t* ring_
   const int ntiles = *a.num_gtiles;
   const int splits = a.nsplit;
   const int units = ntiles * NG * splits;
-  uint32_t* ring = ring_all + wv * ring_words<MG>();
+  uint32_t* ring = ring_all + wv * ring_words<BITS, MG>();
   const uint32_t mask = vreg_const(kMcgMask), orv = kMcgOr;
   for (int u = gw; u < units; u += W) {
     const int s = u % splits;
     const int rest = u / splits;
     const int ng = rest % NG;
     const int4 t = a.gtiles[rest / NG];
-    if constexpr (BITS == 5 || BITS == 6) {
-      unit_f16_wide<BITS, MG>(a, t, ng, s, splits, lane, mask, orv);
-    } else if constexpr (BITS != 0 && BITS != kMixedWide) {
+    if constexpr (BITS != 0 && BITS != kMixedWide) {
       unit_f16<BITS, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
     } else {
       const int bits = (t.x >> 24) & 0xff;
@@ -275,8 +225,8 @@ __device__ __forceinline__ void gemm_f16_body(const GemmArgs& a, uint32_t* ring_
       else if (bits == 3) unit_f16<3, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
       else if (BITS == 0 || bits == 2) unit_f16<2, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
       else if constexpr (BITS == kMixedWide) {
-        if (bits == 5) unit_f16_wide<5, MG>(a, t, ng, s, splits, lane, mask, orv);
-        else unit_f16_wide<6, MG>(a, t, ng, s, splits, lane, mask, orv);
+        if (bits == 5) unit_f16<5, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
+        else unit_f16<6, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
       }
     }
   }
@@ -286,13 +236,13 @@ __device__ __forceinline__ void gemm_f16_body(const GemmArgs& a, uint32_t* ring_
 // units covers the chip evenly.
 template <int BITS, int MG, int FC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 0 || BITS >= 5 ? 3 : 5, 8))) void k_gemm_f16_small(GemmArgs a) {
-  __shared__ uint32_t ring_all[4 * ring_words<MG>()];
+  __shared__ uint32_t ring_all[4 * ring_words<BITS, MG>()];
   gemm_f16_body<BITS, MG, FC>(a, ring_all);
 }
 
 template <int BITS, int MG, int FC>
 __global__ __launch_bounds__(256) void k_gemm_f16(GemmArgs a) {
-  __shared__ uint32_t ring_all[4 * ring_words<MG>()];
+  __shared__ uint32_t ring_all[4 * ring_words<BITS, MG>()];
   gemm_f16_body<BITS, MG, FC>(a, ring_all);
 }
 
