@@ -393,6 +393,7 @@ def main():
         "fc2_gbs": fc2_gbs,
         "gemm_pair_gbs": (b.fc1_bytes + b.fc2_bytes) / ((km["fc1"] + km["fc2"]) * 1e-3) / 1e9,
         "layer_weight_gbs": (b.fc1_bytes + b.fc2_bytes) / (ms * 1e-3) / 1e9,
+        "routes_per_s": b.inp.routes / (ms * 1e-3),
         "replay_us": b.replay_stats(),
         "gemm_activity": stored_busy(args.workload),
     }
@@ -414,7 +415,10 @@ def main():
         out["parity_rel_err"] = float(np.max(np.abs(y - yref)) / np.max(np.abs(yref)))
     if not args.no_extra:
         extra = {}
-        for nm, t, w8 in (("prefill", 2048, False), ("w4a8", 64, True), ("wide", 16, False), ("decode", 1, False)):
+        # every token count of every geometry (the headline decode T=16 is the main line above)
+        for nm, t, w8 in (("prefill", 2048, False), ("w4a8", 64, True), ("w4a8", 32, True), ("w4a8", 8, True),
+                          ("w4a8", 1, True), ("wide", 16, False), ("wide", 512, False), ("decode", 4, False),
+                          ("decode", 1, False)):
             e = Bench(nm, t, w8)
             rr = e.run(max(5, args.steps // 5), 3)
             s2, k2 = rr["stage_ms"], rr["kernel_ms"]
@@ -422,7 +426,8 @@ def main():
             peak = MFMA_F8_PEAK_TFLOPS if w8 else MFMA_F16_PEAK_TFLOPS
             tf = (e.flops_fc1 + e.flops_fc2) / gemm_s / 1e12
             gbs = (e.fc1_bytes + e.fc2_bytes) / gemm_s / 1e9
-            extra[f"{nm}:{t}"] = {"tokens_per_s": t / (rr["ms_step"] * 1e-3), "ms_per_step": rr["ms_step"],
+            extra[f"{nm}:{t}"] = {"tokens_per_s": t / (rr["ms_step"] * 1e-3),
+                                  "routes_per_s": e.inp.routes / (rr["ms_step"] * 1e-3), "ms_per_step": rr["ms_step"],
                                   "gemm_tflops": tf, "gemm_tflops_frac": tf / peak, "gemm_weight_gbs": gbs,
                                   "gemm_weight_gbs_frac": gbs / HBM_PEAK_GBS, "stage_ms": s2, "kernel_ms": k2,
                                   "touched_experts": e.touched, "weight_copies": e.n_copies,
