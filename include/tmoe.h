@@ -62,7 +62,7 @@ typedef enum {
 } tmoe_status;
 
 enum { TMOE_ROT_HADAMARD = 0, TMOE_ROT_IDENTITY = 1 };   /* identity: every R_n = I (test mode) */
-enum { TMOE_IDS_I32 = 0, TMOE_IDS_I64 = 1 };             /* "int32 or int64 ids" (flashinfer PR #69) */
+enum { TMOE_IDS_I32 = 0, TMOE_IDS_I64 = 1 };             /* 32- or 64-bit ids (flashinfer PR #69)  */
 
 typedef struct {
   int32_t hidden;              /* H: multiple of 64, 64..4096; power of two or 128*q (+64)  */

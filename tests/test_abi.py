@@ -1,9 +1,9 @@
 """C ABI checks that need no GPU: exported symbols and fail-closed host validation.
 
-Validation happens before any launch ("fail closed on malformed layouts ... and invalid route
-maps", 'serve canonical Fruit QSRT atoms' (b12x PR #129), Summary; a short or misaligned arena is
-rejected, 'TrellisMX (procedural NPK) ... P8 runtime' (flashinfer PR #69), description), so every
-call below returns before touching a (fake) device pointer."""
+Validation happens before any launch (the Summary of 'serve canonical Fruit QSRT atoms' (b12x PR
+#129) rejects bad layouts and route maps up front; the description of 'TrellisMX (procedural NPK)
+... P8 runtime' (flashinfer PR #69) rejects a short or misaligned arena), so every call below
+returns before touching a (fake) device pointer."""
 import ctypes
 import os
 import re

@@ -1,8 +1,8 @@
 // k_trellis_gemm.hip -- grouped GEMMs over the route map with trellis weights decoded in registers.
 //
 // Weights are never expanded in HBM: each wavefront streams the packed trellis words of its
-// tiles, decodes them straight into MFMA operands ("W4A8 decode expands fixed-stride trellis
-// payload directly into E4M3 MMA operands", "serve canonical Fruit QSRT atoms", Hot path) and
+// tiles, decodes them straight into MFMA operands (the hot path of "serve canonical Fruit QSRT
+// atoms" turns the packed payload into E4M3 matrix operands directly in its W4A8 path) and
 // multiplies them with the route rows of one expert. Output is route-major in slot order, one
 // plane per K split, summed in a fixed order by the consumer kernel (deterministic; no atomics).
 //

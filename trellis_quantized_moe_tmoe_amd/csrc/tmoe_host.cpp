@@ -1,8 +1,8 @@
 // tmoe_host.cpp -- the C ABI: plan validation, scratch layout and the launch sequence.
 //
 // Every argument is checked before the first launch, so a rejected call leaves the caller's
-// output and scratch untouched ("fail closed on malformed layouts ... and invalid route maps",
-// "serve canonical Fruit QSRT atoms", Summary). Plans are host-only; the library allocates
+// output and scratch untouched (the Summary of "serve canonical Fruit QSRT atoms" rejects bad
+// layouts and route maps before any work). Plans are host-only; the library allocates
 // nothing: per-expert payload offsets travel as packed launch arguments and are expanded into the
 // caller's scratch by the route-map kernel, so a forward call can be captured into a hipGraph.
 #include <algorithm>
