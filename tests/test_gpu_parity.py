@@ -392,3 +392,31 @@ def test_graph_capture_replay_with_changed_inputs():
         import dataclasses
         ref = O.forward(dataclasses.replace(c.inp, x_bf16=other.x_bf16, ids=other.ids, weights=other.weights))
         assert rel_err(y.cpu().numpy(), ref) <= TOL_W4A16
+
+
+@pytest.mark.parametrize("name,T,w4a8", [("prefill", 2048, False), ("wide", 512, False), ("w4a8", 64, True)])
+def test_graph_replay_large_batches_and_w4a8(name, T, w4a8):
+    """Graph replays with changed inputs equal eager calls bit for bit: the two-launch route map of
+    large batches (rotation shared between the launches), 128-row tiles, blocked rows, and W4A8."""
+    from trellis_quantized_moe_tmoe_amd.workloads import make_inputs
+    c = Case(name, T)
+    y = torch.empty((T, c.inp.hidden), device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c.plan.forward(c.x, c.ids, c.w, c.weights, c.scratch, y=y, w4a8=w4a8)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        c.plan.forward(c.x, c.ids, c.w, c.weights, c.scratch, y=y, w4a8=w4a8)
+    for seed in (5, 6):
+        other = make_inputs(name, tokens=T, seed=seed)
+        c.x.copy_(torch.from_numpy(other.x_bf16.view(np.int16)).cuda())
+        c.ids.copy_(torch.from_numpy(other.ids).cuda())
+        c.w.copy_(torch.from_numpy(other.weights).cuda())
+        g.replay()
+        torch.cuda.synchronize()
+        eager = c.plan.forward(c.x, c.ids, c.w, c.weights, c.scratch, w4a8=w4a8).clone()
+        torch.cuda.synchronize()
+        say(f"[result] {c.label} replay seed {seed}: max |replay - eager| {float((y - eager).abs().max()):.3e}")
+        assert torch.equal(y, eager)
