@@ -95,6 +95,8 @@ def test_decode_bit_exact_widths_5_6(bits):
 @pytest.mark.parametrize("name,T,over", [
     ("tiny", 4, dict(bits_override=5)),                          # 16-row tiles
     ("tiny", 4, dict(bits_override=6)),
+    ("tiny", 16, dict(bits_override=5)),                         # 32-row tiles (2E < routes <= 8E)
+    ("tiny", 16, dict(bits_choices=(2, 3, 4, 5, 6))),            # 32-row tiles, mixed 2-6
     ("decode", 16, dict(bits_override=6)),
     ("tiny", 300, dict(bits_override=5)),                        # 64-row tiles (no 128-row tiles at 5-6)
     ("tiny", 40, dict(bits_choices=(2, 3, 4, 5, 6))),            # mixed 2-6, 64-row tiles
