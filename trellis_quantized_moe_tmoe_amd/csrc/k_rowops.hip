@@ -250,14 +250,18 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
   for (int it = 0; it < rounds; ++it) {
     const int j = it * W + wv;
     const int r = t * K + j;
-    const int p = j < K ? a.route_slot[r] : -1;
+    // the route's expert and weight do not depend on its slot, so their loads go out with the slot's
+    const bool jk = j < K;
+    const int p = jk ? a.route_slot[r] : -1;
+    const int e_r = jk ? static_cast<int>(route_expert(a.ids, a.ids64, r)) : 0;
+    const float w_r = jk ? a.w[r] : 0.0f;
     if (lane == 0) live[wv] = p >= 0;
     if (p >= 0) {
-      const int e = static_cast<int>(route_expert(a.ids, a.ids64, r));
+      const int e = e_r;
       // S values per lane in registers: split sum, scale, rotation, sign and weight, one LDS write
       auto in_registers = [&](auto s_const) {
         constexpr int S = decltype(s_const)::value;
-        const float wt = a.w[r];
+        const float wt = w_r;
         float vv[S];
         sum_splits<S, SMAX, splits_unroll<S, SMAX>(1)>(a.v + static_cast<size_t>(p) * H + off + lane, plane, splits, vv);
         const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + off + lane;
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
 #pragma unroll
           for (int i = 0; i < U; ++i) row[base + 64 * i + lane] = sum[i] * h2f(c2[base + 64 * i]);
         }
-        CombineRotBody body{a, row, lane, e, a.w[r]};
+        CombineRotBody body{a, row, lane, e, w_r};
         for_segments<EPL>(a.rot, body);
       }
     }
@@ -326,8 +330,9 @@ __device__ __forceinline__ void combine_block(const CombineArgs& a, int t, int o
   const size_t plane = static_cast<size_t>(a.routes) * H;
   const int rl = t * K + (lane < K ? lane : K - 1);
   const int p_l = lane < K ? a.route_slot[rl] : -1;
-  const int e_l = p_l >= 0 ? static_cast<int>(route_expert(a.ids, a.ids64, rl)) : 0;
-  const float w_l = p_l >= 0 ? a.w[rl] : 0.0f;
+  // expert and weight loads do not wait for the slot's (a dropped route's are never used)
+  const int e_l = lane < K ? static_cast<int>(route_expert(a.ids, a.ids64, rl)) : 0;
+  const float w_l = lane < K ? a.w[rl] : 0.0f;
   float acc[S];
 #pragma unroll
   for (int i = 0; i < S; ++i) acc[i] = 0.0f;
@@ -338,7 +343,7 @@ __device__ __forceinline__ void combine_block(const CombineArgs& a, int t, int o
     for (int jb = 0; jb < JB; ++jb) {
       const int j = j0 + jb < K ? j0 + jb : K - 1;
       p[jb] = j0 + jb < K ? __builtin_amdgcn_readlane(p_l, j) : -1;
-      const int e = __builtin_amdgcn_readlane(e_l, j);
+      const int e = p[jb] >= 0 ? __builtin_amdgcn_readlane(e_l, j) : 0;   // a dropped route's id may be invalid
       const int pp = p[jb] >= 0 ? p[jb] : 0;
       sum_splits<S, SMAX, SMAX>(a.v + static_cast<size_t>(pp) * H + off + lane, plane, SMAX, vv[jb]);
       const uint16_t* cs = a.scale2 + static_cast<size_t>(e) * H + off + lane;
