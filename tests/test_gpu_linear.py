@@ -49,6 +49,8 @@ class LinearCase:
     ("linear", 16, dict(bits=3)),
     ("linear", 16, dict(bits=5)),                                  # two half windows per 8-element group
     ("linear", 300, dict(bits=6, in_features=512, out_features=256)),  # 64-row tiles at widths 5-6
+    ("linear", 16, dict(in_features=2048, out_features=4096)),     # rows of 2048 and 4096 values: both
+    ("linear", 5, dict(in_features=4096, out_features=1024, bits=3)),  # rotations split over a workgroup
     ("linear_wide", 16, {}),                                       # 2560 x 320, 3-bit, both rotations blocked
     ("linear_wide", 2100, dict(in_features=320, out_features=2560)),   # many tokens: per-route rotation,
                                                                    # per-block combine wavefronts
@@ -63,6 +65,11 @@ def test_linear_matches_oracle(name, T, over):
 def test_linear_identity_mode_and_capacity_above_T():
     c = LinearCase("linear", 24, max_tokens=512, rotation="identity", identity_signs=True,
                    in_features=128, out_features=256)
+    assert rel_err(c.run().cpu().numpy(), c.oracle()) <= TOL_LINEAR
+
+
+def test_linear_identity_mode_long_rows():
+    c = LinearCase("linear", 9, rotation="identity", identity_signs=True, in_features=4096, out_features=2048)
     assert rel_err(c.run().cpu().numpy(), c.oracle()) <= TOL_LINEAR
 
 

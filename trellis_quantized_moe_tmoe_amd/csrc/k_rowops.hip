@@ -406,6 +406,107 @@ __global__ __launch_bounds__(256) void k_linear_prep(LinearPrepArgs a) {
   if (i0 == 0) *a.num_gtiles = nt;
 }
 
+// Long power-of-two rows (n = 256 B with B = 4, 8, 16, i.e. 1024-4096 values) split over a workgroup
+// of n/4 threads: wavefront w first transforms its contiguous 256 values (4 per lane; index bits 0-7,
+// fwht_segment<4>), the block goes through LDS, and 256 threads then each hold the B values that
+// share index bits 0-7 and transform index bits 8 and up in registers. The two passes cover every
+// index bit once, so this is the same n-point Walsh-Hadamard transform, with 1/sqrt(n) applied as
+// 1/16 and then 1/sqrt(B). A wavefront per row would walk 64 values per lane through twelve stages.
+template <int B>
+__device__ __forceinline__ void fwht_across_blocks(float (&u)[B]) {
+#pragma unroll
+  for (int h = 1; h < B; h <<= 1)
+#pragma unroll
+    for (int m = 0; m < B; ++m)
+      if ((m & h) == 0) {
+        const float x0 = u[m], x1 = u[m | h];
+        u[m] = x0 + x1;
+        u[m | h] = x0 - x1;
+      }
+  constexpr float kScale = B == 4 ? 0.5f : B == 8 ? 0.35355339059327373f : 0.25f;   // 1/sqrt(B)
+#pragma unroll
+  for (int m = 0; m < B; ++m) u[m] *= kScale;
+}
+
+// Dense linear input rotation with workgroup rows: workgroups [0, tokens) rotate row t (operand row
+// t, sign vector su); the rest write the GEMM tiles and the combine's route tables.
+template <int B>
+__global__ __launch_bounds__(64 * B) void k_linear_prep_wide(LinearPrepArgs a) {
+  __shared__ float row[256 * B];
+  const RotateArgs& r = a.rot;
+  if (static_cast<int>(blockIdx.x) < a.tokens) {
+    const int t = blockIdx.x, n = 256 * B;
+    const int lane = threadIdx.x & 63, off = static_cast<int>(threadIdx.x >> 6) * 256 + lane;
+    const uint16_t* xr = r.x + static_cast<size_t>(t) * n + off;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = bf16_to_f32(xr[64 * i]) * h2f(r.su1[off + 64 * i]);
+    if (!r.rot.identity) fwht_segment<4>(v, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) row[off + 64 * i] = v[i];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      float u[B];
+#pragma unroll
+      for (int m = 0; m < B; ++m) u[m] = row[threadIdx.x + 256 * m];
+      if (!r.rot.identity) fwht_across_blocks<B>(u);
+      _Float16* o = static_cast<_Float16*>(r.a1) + static_cast<size_t>(t) * r.lda + threadIdx.x;
+#pragma unroll
+      for (int m = 0; m < B; ++m) o[256 * m] = static_cast<_Float16>(u[m]);
+    }
+    return;
+  }
+  const int i0 = (static_cast<int>(blockIdx.x) - a.tokens) * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x);
+  const int stride = (static_cast<int>(gridDim.x) - a.tokens) * static_cast<int>(blockDim.x);
+  for (int i = i0; i < a.tokens; i += stride) {
+    a.slot[i] = i;
+    a.ids[i] = 0;
+    a.w[i] = 1.0f;
+  }
+  const int nt = (a.tokens + a.tile_rows - 1) / a.tile_rows;
+  for (int i = i0; i < nt; i += stride)
+    a.gtiles[i] = make_int4(a.bits << 24, i * a.tile_rows, min(a.tile_rows, a.tokens - i * a.tile_rows), 0);
+  if (i0 == 0) *a.num_gtiles = nt;
+}
+
+// Combine of one route per token (top-k = 1, the dense linear's case) with workgroup rows:
+// y_t = w[t] * sv2_e * R_n(scale2_e * v_slot), or zeros for a dropped route; one workgroup per token.
+template <int B, int SMAX>
+__global__ __launch_bounds__(64 * B) void k_combine_one_wide(CombineArgs a) {
+  __shared__ float row[256 * B];
+  const int t = blockIdx.x, n = 256 * B;
+  const int lane = threadIdx.x & 63, off = static_cast<int>(threadIdx.x >> 6) * 256 + lane;
+  const int p = a.route_slot[t];
+  const long long id = route_expert(a.ids, a.ids64, t);
+  const float wt = a.w[t];
+  const int e = p >= 0 ? static_cast<int>(id) : 0;
+  float v[4];
+  if (p >= 0) {
+    const size_t plane = static_cast<size_t>(a.routes) * n;
+    sum_splits<4, SMAX, splits_unroll<4, SMAX>(1)>(a.v + static_cast<size_t>(p) * n + off, plane, SMAX, v);
+    const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * n + off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] *= h2f(c2[64 * i]);
+    if (!a.rot.identity) fwht_segment<4>(v, lane);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) row[off + 64 * i] = v[i];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    float u[B];
+#pragma unroll
+    for (int m = 0; m < B; ++m) u[m] = row[threadIdx.x + 256 * m];
+    if (p >= 0 && !a.rot.identity) fwht_across_blocks<B>(u);
+    const uint16_t* sg = a.sv2 + static_cast<size_t>(e) * n + threadIdx.x;
+    float* y = a.y + static_cast<size_t>(t) * n + threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < B; ++m) y[256 * m] = p >= 0 ? wt * (u[m] * h2f(sg[256 * m])) : 0.0f;
+  }
+}
+
 struct DebugRotateBody {
   float* row;
   const RowRot& rot;
@@ -490,7 +591,21 @@ void launch_act(const ActArgs& a, bool mx, hipStream_t s) {
   });
 }
 
+// Rows split over a workgroup: power-of-two rows of 1024 to 4096 values (B = n / 256).
+static int wide_rows_b(const RowRot& r) { return r.pow2 && r.n >= 1024 && r.n <= 4096 ? r.n / 256 : 0; }
+
 void launch_combine(const CombineArgs& a, hipStream_t s) {
+  if (a.top_k == 1 && wide_rows_b(a.rot) != 0) {
+    dispatch_smax(a.nsplit, [&](auto sm) {
+      constexpr int SM = decltype(sm)::value;
+      switch (wide_rows_b(a.rot)) {
+        case 4: hipLaunchKernelGGL((k_combine_one_wide<4, SM>), dim3(a.tokens), dim3(256), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((k_combine_one_wide<8, SM>), dim3(a.tokens), dim3(512), 0, s, a); break;
+        default: hipLaunchKernelGGL((k_combine_one_wide<16, SM>), dim3(a.tokens), dim3(1024), 0, s, a); break;
+      }
+    });
+    return;
+  }
   if (!a.rot.pow2 && !a.split_segments) {
     const unsigned grid = blocks_for(static_cast<long long>(a.tokens) * row_segments(a.rot));
     dispatch_smax(a.nsplit, [&](auto sm) {
@@ -512,6 +627,14 @@ void launch_combine(const CombineArgs& a, hipStream_t s) {
 }
 
 void launch_linear_prep(const LinearPrepArgs& a, hipStream_t s) {
+  if (const int b = wide_rows_b(a.rot.rot)) {
+    const int meta = std::max(1, std::min(64, (a.tokens + 64 * b - 1) / (64 * b)));
+    const dim3 grid(a.tokens + meta);
+    if (b == 4) hipLaunchKernelGGL((k_linear_prep_wide<4>), grid, dim3(256), 0, s, a);
+    else if (b == 8) hipLaunchKernelGGL((k_linear_prep_wide<8>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((k_linear_prep_wide<16>), grid, dim3(1024), 0, s, a);
+    return;
+  }
   const int meta = std::max(1, std::min(64, (a.tokens + 255) / 256));
   const dim3 grid(a.rot_blocks + meta);
   dispatch_epl(a.rot.rot, [&](auto epl) {
