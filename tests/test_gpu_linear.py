@@ -90,9 +90,10 @@ def test_linear_zero_tokens_leaves_y():
     assert torch.all(y == 7.0)
 
 
-def test_linear_graph_replay_with_changed_inputs():
-    c = LinearCase("linear", 16, in_features=256, out_features=256)
-    y = torch.empty((16, 256), device="cuda")
+@pytest.mark.parametrize("n", [256, 4096])      # 4096: workgroup-row rotations on both sides
+def test_linear_graph_replay_with_changed_inputs(n):
+    c = LinearCase("linear", 16, in_features=n, out_features=n)
+    y = torch.empty((16, n), device="cuda")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -104,7 +105,7 @@ def test_linear_graph_replay_with_changed_inputs():
         c.plan.forward(c.x, c.w, c.scratch, y=y)
     torch.cuda.synchronize()
     for seed in (11, 12, 13):
-        other = make_linear_inputs("linear", tokens=16, seed=seed, in_features=256, out_features=256)
+        other = make_linear_inputs("linear", tokens=16, seed=seed, in_features=n, out_features=n)
         c.x.copy_(torch.from_numpy(other.x_bf16.view(np.int16).copy()))
         g.replay()
         torch.cuda.synchronize()
