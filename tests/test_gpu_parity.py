@@ -209,8 +209,8 @@ def test_layer_w4a16_workgroup_tile_edges(name, T, over):
     assert err <= TOL_W4A16
 
 
-@pytest.mark.parametrize("hidden", [1024, 2048, 4096])
-def test_layer_top1_long_rows_with_a_dropped_route(hidden):
+@pytest.mark.parametrize("hidden,w4a8", [(1024, False), (2048, False), (4096, False), (2048, True)])
+def test_layer_top1_long_rows_with_a_dropped_route(hidden, w4a8):
     # top-k = 1 with output rows of 1024-4096 values: the combine splits each row over a workgroup;
     # token 2's only route has an invalid id, so its output row is zero
     import dataclasses
@@ -218,15 +218,15 @@ def test_layer_top1_long_rows_with_a_dropped_route(hidden):
     ids = c.inp.ids.copy()
     ids[2, 0] = -1
     c.ids = torch.from_numpy(ids).cuda()
-    y = c.run().cpu().numpy()
+    y = c.run(w4a8=w4a8).cpu().numpy()
     w = c.inp.weights.copy()
     w[2, 0] = 0.0
     fixed = ids.copy()
     fixed[2, 0] = 0
-    ref = O.forward(dataclasses.replace(c.inp, ids=fixed, weights=w))
-    say(f"[result] {c.label} top-1 rel err {rel_err(y, ref):.3e}")
+    ref = O.forward(dataclasses.replace(c.inp, ids=fixed, weights=w), mode="w4a8" if w4a8 else "w4a16")
+    say(f"[result] {c.label} top-1 {'W4A8' if w4a8 else 'W4A16'} rel err {rel_err(y, ref):.3e}")
     assert np.all(y[2] == 0.0)
-    assert rel_err(y, ref) <= TOL_W4A16
+    assert rel_err(y, ref) <= (TOL_W4A8_EMU if w4a8 else TOL_W4A16)
 
 
 def test_w4a16_path_on_w4a8_geometry():
