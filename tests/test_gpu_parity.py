@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle_np as O
-from gpu_cases import TOL_W4A16, TOL_W4A8_EMU, Case, e4m3_of_fp16_table, rel_err, say
+from gpu_cases import TOL_W4A16, TOL_W4A8, TOL_W4A8_EMU, Case, e4m3_of_fp16_table, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -153,9 +153,14 @@ def test_layer_w4a8(T):
     y = c.run(w4a8=True).cpu().numpy()
     err_emu = rel_err(y, c.oracle_w4a8)
     err_16 = rel_err(y, c.oracle_w4a16)
-    say(f"[result] {c.label} W4A8 rel err vs W4A8 oracle {err_emu:.3e}, vs W4A16 oracle {err_16:.3e}")
+    gap = rel_err(c.oracle_w4a8, c.oracle_w4a16)
+    say(f"[result] {c.label} W4A8 rel err vs W4A8 oracle {err_emu:.3e}, vs W4A16 oracle {err_16:.3e} "
+        f"(the oracle's own W4A8-to-W4A16 gap {gap:.3e}; stated bound {TOL_W4A8:.0e})")
     assert err_emu <= TOL_W4A8_EMU
-    assert err_16 <= 0.12     # measured, not the 3e-2 target: E4M3 operands carry ~2.6% RMS each
+    # Against the W4A16 oracle the GPU can be off by at most the oracle's own gap between its two
+    # modes (5.2e-2 to 7.7e-2 here: each of the four E4M3 operands carries ~2.6% RMS rounding) plus
+    # the emulation bound above; the stated 3e-2 is not met by the W4A8 definition itself.
+    assert err_16 <= gap + TOL_W4A8_EMU
 
 
 @pytest.mark.parametrize("over", [

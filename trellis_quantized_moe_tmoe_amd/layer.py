@@ -22,6 +22,40 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+# The C ABI sees raw pointers only, so it cannot check buffer sizes: the shapes, dtypes, layouts
+# and devices of the tensors are checked here, before any call that would launch a kernel.
+_BITS16 = (torch.int16, torch.bfloat16, torch.uint16) if hasattr(torch, "uint16") else (torch.int16, torch.bfloat16)
+
+
+def _require(t, name: str, shape, dtypes) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _same_device(named) -> None:
+    devs = {t.device for _, t in named}
+    if len(devs) != 1:
+        raise ValueError("tensors on different devices: " + ", ".join(f"{n}={t.device}" for n, t in named))
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {dev}")
+
+
+def _check_scratch(scratch, need: int) -> None:
+    if not isinstance(scratch, torch.Tensor) or scratch.dtype != torch.uint8 or scratch.dim() != 1:
+        raise ValueError("scratch: expected a 1-D uint8 tensor")
+    if not scratch.is_contiguous():
+        raise ValueError("scratch: must be contiguous")
+    if scratch.numel() < need:
+        raise ValueError(f"scratch: {scratch.numel()} bytes, the plan needs {need}")
+
+
 class DeviceWeights:
     """Device copies of one weight set: trellis payload words, fp16 scales and sign vectors."""
 
@@ -105,9 +139,10 @@ class Plan:
 
     def forward(self, x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor, weights: DeviceWeights,
                 scratch: torch.Tensor, y: Optional[torch.Tensor] = None, w4a8: bool = False) -> torch.Tensor:
-        T = x.shape[0]
-        if y is None:
-            y = torch.empty((T, self.hidden), dtype=torch.float32, device=x.device)
+        T = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+        if y is None and isinstance(x, torch.Tensor):
+            y = torch.empty((max(T, 0), self.hidden), dtype=torch.float32, device=x.device)
+        self.check_call(x, ids, w, weights, scratch, y)
         fn = lib.tmoe_forward_w4a8 if w4a8 else lib.tmoe_forward_w4a16
         check(fn(self.handle, _ptr(x), _ptr(ids), _ptr(w), T, ctypes.byref(weights.c), _ptr(y), _ptr(scratch),
                  scratch.numel(), _stream(x.device)), "tmoe_forward_w4a8" if w4a8 else "tmoe_forward_w4a16")
@@ -115,9 +150,33 @@ class Plan:
 
     def forward_stages(self, first: int, last: int, x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor,
                        weights: DeviceWeights, scratch: torch.Tensor, y: torch.Tensor, w4a8: bool = False) -> None:
+        self.check_call(x, ids, w, weights, scratch, y)
         check(lib.tmoe_forward_stages(self.handle, int(w4a8), first, last, _ptr(x), _ptr(ids), _ptr(w), x.shape[0],
                                       ctypes.byref(weights.c), _ptr(y), _ptr(scratch), scratch.numel(),
                                       _stream(x.device)), "tmoe_forward_stages")
+
+    def check_call(self, x, ids, w, weights, scratch, y) -> None:
+        """Raise ValueError unless the tensors match what the forward reads and writes: x bf16 bits
+        [T, H]; ids [T, k] of the plan's id dtype; w fp32 [T, k]; y fp32 [T, H]; weights of this
+        plan's shapes; scratch at least the planned bytes; all contiguous, on one GPU device."""
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError("x: expected a 2-D tensor [T, H]")
+        T = x.shape[0]
+        if T > self.max_tokens:
+            raise ValueError(f"x: {T} tokens, the plan holds at most {self.max_tokens}")
+        H, I, E, k = self.hidden, self.inter, self.num_experts, self.top_k
+        _require(x, "x", (T, H), _BITS16)
+        _require(ids, "ids", (T, k), (self.ids_dtype,))
+        _require(w, "w", (T, k), (torch.float32,))
+        _require(y, "y", (T, H), (torch.float32,))
+        if not isinstance(weights, DeviceWeights):
+            raise ValueError("weights: expected DeviceWeights")
+        _require(weights.payload, "payload", (self.payload_words,), (torch.int16,))
+        for name, n in (("scale1", 2 * I), ("scale2", H), ("su1", H), ("sv1", 2 * I), ("su2", I), ("sv2", H)):
+            _require(getattr(weights, name), name, (E, n), (torch.float16, torch.int16))
+        _check_scratch(scratch, self.scratch_bytes)
+        _same_device([("x", x), ("ids", ids), ("w", w), ("y", y), ("scratch", scratch)] +
+                     [(n, getattr(weights, n)) for n in DeviceWeights.FIELDS])
 
     def forward_status(self, x, ids, w, T, weights, y, scratch, scratch_bytes, w4a8=False, stream=None) -> int:
         """Raw status of a forward call with explicit (possibly invalid) arguments; for tests."""
@@ -230,12 +289,33 @@ class LinearPlan:
 
     def forward(self, x: torch.Tensor, weights: LinearWeightsDev, scratch: torch.Tensor,
                 y: Optional[torch.Tensor] = None) -> torch.Tensor:
-        T = x.shape[0]
-        if y is None:
-            y = torch.empty((T, self.out_features), dtype=torch.float32, device=x.device)
+        T = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+        if y is None and isinstance(x, torch.Tensor):
+            y = torch.empty((max(T, 0), self.out_features), dtype=torch.float32, device=x.device)
+        self.check_call(x, weights, scratch, y)
         check(lib.tmoe_linear_w4a16(self.handle, _ptr(x), T, ctypes.byref(weights.c), _ptr(y), _ptr(scratch),
                                     scratch.numel(), _stream(x.device)), "tmoe_linear_w4a16")
         return y
+
+    def check_call(self, x, weights, scratch, y) -> None:
+        """Raise ValueError unless x is bf16 bits [T, K], y fp32 [T, N], the weights match the plan
+        and scratch holds the planned bytes, all contiguous on one GPU device."""
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError("x: expected a 2-D tensor [T, K]")
+        T = x.shape[0]
+        if T > self.max_tokens:
+            raise ValueError(f"x: {T} tokens, the plan holds at most {self.max_tokens}")
+        K, N = self.in_features, self.out_features
+        _require(x, "x", (T, K), _BITS16)
+        _require(y, "y", (T, N), (torch.float32,))
+        if not isinstance(weights, LinearWeightsDev):
+            raise ValueError("weights: expected LinearWeightsDev")
+        _require(weights.payload, "payload", (self.payload_words,), (torch.int16,))
+        for name, n in (("scale", N), ("su", K), ("sv", N)):
+            _require(getattr(weights, name), name, (n,), (torch.float16, torch.int16))
+        _check_scratch(scratch, self.scratch_bytes)
+        _same_device([("x", x), ("y", y), ("scratch", scratch)] +
+                     [(n, getattr(weights, n)) for n in LinearWeightsDev.FIELDS])
 
     def forward_status(self, x, T, weights, y, scratch, scratch_bytes, stream=None) -> int:
         """Raw status of a call with explicit (possibly invalid) arguments; for tests."""
