@@ -71,7 +71,8 @@ class Probe:
         codes = self.expert(e)[matrix][k]
         if not self.w4a8:
             return codes.view(np.float16).astype(np.float32)
-        return _e4m3_value(self.lut[codes])
+        # a small negative code rounds to E4M3 -0, which the exact fp32 sum 0 + (-0) * 1 makes +0
+        return _e4m3_value(self.lut[codes]) + np.float32(0.0)
 
     def check(self, matrix: int, salt: int) -> int:
         """FC1 (matrix 0) or FC2 (matrix 1) on one-hot rows; returns the number of rows compared."""
