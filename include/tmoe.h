@@ -58,8 +58,12 @@ typedef enum {
   TMOE_ERR_SCRATCH = 3,       /* scratch shorter than planned, or not 16-byte aligned */
   TMOE_ERR_CAPACITY = 4,      /* T > max_tokens of the plan */
   TMOE_ERR_ALIGNMENT = 5,     /* a device pointer not aligned as documented */
-  TMOE_ERR_HIP = 6            /* a HIP launch reported an error */
+  TMOE_ERR_HIP = 6,           /* a HIP launch reported an error */
+  TMOE_ERR_STATIC_SCRATCH = 7 /* plan needs more than TMOE_STATIC_SCRATCH_BYTES (static entry point) */
 } tmoe_status;
+
+/* Size of the library-owned scratch arena of tmoe_forward_w4a16_static, per GPU (32 MiB). */
+#define TMOE_STATIC_SCRATCH_BYTES (32u << 20)
 
 enum { TMOE_ROT_HADAMARD = 0, TMOE_ROT_IDENTITY = 1 };   /* identity: every R_n = I (test mode) */
 enum { TMOE_IDS_I32 = 0, TMOE_IDS_I64 = 1 };             /* 32- or 64-bit ids (flashinfer PR #69)  */
@@ -139,6 +143,22 @@ tmoe_status tmoe_forward_w4a16(tmoe_plan_t plan, const void *x_bf16, const void 
 tmoe_status tmoe_forward_w4a8(tmoe_plan_t plan, const void *x_bf16, const void *topk_ids,
                               const float *topk_w, int32_t T, const tmoe_weights *weights,
                               float *y, void *scratch, size_t scratch_bytes, void *stream);
+
+/* tmoe_forward_w4a16 for callers that cannot allocate device memory (code under hipGraph capture,
+ * tight serving loops, harnesses that forbid allocation): no scratch argument; the arena is a
+ * device array of TMOE_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on, from
+ * the first call on that GPU until the process ends. The call itself allocates nothing (the
+ * array's device address is looked up once per GPU, on the first call there). Plans whose
+ * scratch_bytes exceed TMOE_STATIC_SCRATCH_BYTES are rejected with TMOE_ERR_STATIC_SCRATCH before
+ * anything is enqueued (a decode plan of H = 1024, I = 512, E = 96, top-8 needs 4.4 MiB at
+ * max_tokens = 16 and 13.8 MiB at 64). Same kernels, same results, same checks as
+ * tmoe_forward_w4a16. Every call on one GPU shares that GPU's array, whose contents are left by
+ * the last call (no call reads a byte it has not written earlier in that call), so two calls that
+ * overlap in time on one GPU -- on different streams, or from different threads -- race and must
+ * not be issued. */
+tmoe_status tmoe_forward_w4a16_static(tmoe_plan_t plan, const void *x_bf16, const void *topk_ids,
+                                      const float *topk_w, int32_t T, const tmoe_weights *weights,
+                                      float *y, void *stream);
 
 /* Run only stages first..last (0 route map with the input rotation + quantize, 1 FC1,
  * 2 activation, 3 FC2, 4 output rotation + combine) of tmoe_forward_w4a16 (w4a8 = 0) or

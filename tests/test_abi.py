@@ -199,3 +199,18 @@ def test_w4a8_rejects_widths_above_four(N):
     args = [h, fake, fake, fake, 4, ctypes.byref(w), fake, fake, sb, None]
     assert N.lib.tmoe_forward_w4a8(*args) == 2
     N.lib.tmoe_plan_destroy(h)
+
+
+def test_static_entry_point_rejects_plans_beyond_its_arena(N):
+    # prefill capacity (2048 tokens, top-8) needs about 184 MiB of scratch: rejected on the host
+    # before any HIP call, so this runs without a GPU
+    st, h, sb, _ = _plan(N, [4] * 96, max_tokens=2048)
+    assert st == 0 and sb > N.STATIC_SCRATCH_BYTES
+    w = N.Weights(*([16] * 7))
+    assert N.lib.tmoe_forward_w4a16_static(h, 16, 16, 16, 4, ctypes.byref(w), 16, None) == 7
+    assert N.lib.tmoe_status_str(7).decode().startswith("plan needs more scratch")
+    st2, h2, sb2, _ = _plan(N, [4] * 96, max_tokens=16)
+    assert st2 == 0 and sb2 <= N.STATIC_SCRATCH_BYTES
+    # T = 0 returns at once, before the device lookup
+    assert N.lib.tmoe_forward_w4a16_static(h2, 16, 16, 16, 0, ctypes.byref(w), 16, None) == 0
+    assert N.lib.tmoe_plan_destroy(h) == 0 and N.lib.tmoe_plan_destroy(h2) == 0

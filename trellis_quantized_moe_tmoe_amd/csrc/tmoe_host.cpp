@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -360,6 +361,33 @@ bool dim_ok(int n) { return n >= 64 && n <= kMaxDim && n % 64 == 0; }
 
 }  // namespace
 
+// ---------------------------------------------------------------- library-owned scratch
+// One arena per GPU for callers that cannot allocate. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per device with the device
+// current and only that address is ever passed on.
+static __device__ __align__(256) uint8_t scratch[TMOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_static_mu;
+std::vector<void*> g_static_ptr;       // device address of `scratch`, per device id (null: not yet)
+
+tmoe_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TMOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (static_cast<int>(g_static_ptr.size()) <= dev) g_static_ptr.resize(dev + 1, nullptr);
+  if (!g_static_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TMOE_ERR_HIP;
+    g_static_ptr[dev] = ptr;
+  }
+  *out = g_static_ptr[dev];
+  return TMOE_OK;
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------- dense trellis linear
 // y_t = sv * R_N(scale * (C^T R_K(su * x_t))): the layer's input rotation, one trellis matrix (as
 // the grouped GEMM of a single expert whose tiles hold every token) and the layer's output
@@ -573,6 +601,17 @@ tmoe_status tmoe_forward_w4a8(tmoe_plan_t p, const void* x, const void* ids, con
   return forward(p, x, ids, w, T, wt, y, scratch, bytes, stream, true);
 }
 
+tmoe_status tmoe_forward_w4a16_static(tmoe_plan_t p, const void* x, const void* ids, const float* w, int32_t T,
+                                      const tmoe_weights* wt, float* y, void* stream) {
+  if (!p) return TMOE_ERR_INVALID_ARG;
+  if (p->lay.total > TMOE_STATIC_SCRATCH_BYTES) return TMOE_ERR_STATIC_SCRATCH;
+  if (T == 0) return forward(p, x, ids, w, T, wt, y, nullptr, 0, stream, false);
+  void* arena = nullptr;
+  const tmoe_status st = static_scratch(&arena);
+  if (st != TMOE_OK) return st;
+  return forward(p, x, ids, w, T, wt, y, arena, TMOE_STATIC_SCRATCH_BYTES, stream, false);
+}
+
 tmoe_status tmoe_forward_stages(tmoe_plan_t p, int32_t w4a8, int32_t first, int32_t last, const void* x,
                                 const void* ids, const float* w, int32_t T, const tmoe_weights* wt, float* y,
                                 void* scratch, size_t bytes, void* stream) {
@@ -589,6 +628,7 @@ const char* tmoe_status_str(tmoe_status s) {
     case TMOE_ERR_CAPACITY: return "token count above the planned capacity";
     case TMOE_ERR_ALIGNMENT: return "device pointer misaligned";
     case TMOE_ERR_HIP: return "HIP launch error";
+    case TMOE_ERR_STATIC_SCRATCH: return "plan needs more scratch than the library's static arena holds";
   }
   return "unknown status";
 }

@@ -148,6 +148,21 @@ class Plan:
                  scratch.numel(), _stream(x.device)), "tmoe_forward_w4a8" if w4a8 else "tmoe_forward_w4a16")
         return y
 
+    def forward_static(self, x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor, weights: DeviceWeights,
+                       y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """W4A16 forward on the library's own per-GPU scratch array (tmoe_forward_w4a16_static): the
+        call allocates nothing when y is given."""
+        T = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+        if y is None and isinstance(x, torch.Tensor):
+            y = torch.empty((max(T, 0), self.hidden), dtype=torch.float32, device=x.device)
+        if self.scratch_bytes > native.STATIC_SCRATCH_BYTES:
+            raise ValueError(f"plan needs {self.scratch_bytes} scratch bytes, the static arena holds "
+                             f"{native.STATIC_SCRATCH_BYTES}")
+        self.check_call(x, ids, w, weights, None, y)
+        check(lib.tmoe_forward_w4a16_static(self.handle, _ptr(x), _ptr(ids), _ptr(w), T, ctypes.byref(weights.c),
+                                            _ptr(y), _stream(x.device)), "tmoe_forward_w4a16_static")
+        return y
+
     def forward_stages(self, first: int, last: int, x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor,
                        weights: DeviceWeights, scratch: torch.Tensor, y: torch.Tensor, w4a8: bool = False) -> None:
         self.check_call(x, ids, w, weights, scratch, y)
@@ -174,9 +189,10 @@ class Plan:
         _require(weights.payload, "payload", (self.payload_words,), (torch.int16,))
         for name, n in (("scale1", 2 * I), ("scale2", H), ("su1", H), ("sv1", 2 * I), ("su2", I), ("sv2", H)):
             _require(getattr(weights, name), name, (E, n), (torch.float16, torch.int16))
-        _check_scratch(scratch, self.scratch_bytes)
-        _same_device([("x", x), ("ids", ids), ("w", w), ("y", y), ("scratch", scratch)] +
-                     [(n, getattr(weights, n)) for n in DeviceWeights.FIELDS])
+        if scratch is not None:
+            _check_scratch(scratch, self.scratch_bytes)
+        _same_device([("x", x), ("ids", ids), ("w", w), ("y", y)] + ([("scratch", scratch)] if scratch is not None else [])
+                     + [(n, getattr(weights, n)) for n in DeviceWeights.FIELDS])
 
     def forward_status(self, x, ids, w, T, weights, y, scratch, scratch_bytes, w4a8=False, stream=None) -> int:
         """Raw status of a forward call with explicit (possibly invalid) arguments; for tests."""

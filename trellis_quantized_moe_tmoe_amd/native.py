@@ -12,13 +12,16 @@ LIB_PATH = os.path.join(HERE, "libtmoe.so")
 
 TMOE_OK = 0
 STATUS_NAMES = {0: "TMOE_OK", 1: "TMOE_ERR_INVALID_ARG", 2: "TMOE_ERR_UNSUPPORTED", 3: "TMOE_ERR_SCRATCH",
-                4: "TMOE_ERR_CAPACITY", 5: "TMOE_ERR_ALIGNMENT", 6: "TMOE_ERR_HIP"}
+                4: "TMOE_ERR_CAPACITY", 5: "TMOE_ERR_ALIGNMENT", 6: "TMOE_ERR_HIP",
+                7: "TMOE_ERR_STATIC_SCRATCH"}
+STATIC_SCRATCH_BYTES = 32 << 20
 ROT_HADAMARD, ROT_IDENTITY = 0, 1
 IDS_I32, IDS_I64 = 0, 1
 
 # every symbol declared in include/tmoe.h
 EXPORTS = ["tmoe_plan", "tmoe_plan_destroy", "tmoe_plan_get_info", "tmoe_plan_expert_offset",
-           "tmoe_build_route_map", "tmoe_forward_w4a16", "tmoe_forward_w4a8", "tmoe_forward_stages",
+           "tmoe_build_route_map", "tmoe_forward_w4a16", "tmoe_forward_w4a8", "tmoe_forward_w4a16_static",
+           "tmoe_forward_stages",
            "tmoe_status_str",
            "tmoe_debug_decode", "tmoe_debug_mxfp8", "tmoe_debug_rotate", "tmoe_debug_get_views",
            "tmoe_linear_plan", "tmoe_linear_plan_destroy", "tmoe_linear_w4a16"]
@@ -87,6 +90,7 @@ def _load():
     fwd = [P, P, P, P, I32, ctypes.POINTER(Weights), P, P, SZ, P]
     lib.tmoe_forward_w4a16.argtypes = fwd
     lib.tmoe_forward_w4a8.argtypes = fwd
+    lib.tmoe_forward_w4a16_static.argtypes = [P, P, P, P, I32, ctypes.POINTER(Weights), P, P]
     lib.tmoe_forward_stages.argtypes = [P, I32, I32, I32, P, P, P, I32, ctypes.POINTER(Weights), P, P, SZ, P]
     lib.tmoe_status_str.argtypes = [I32]
     lib.tmoe_status_str.restype = ctypes.c_char_p
