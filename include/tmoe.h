@@ -78,7 +78,18 @@ typedef struct {
   int32_t rotation;            /* TMOE_ROT_HADAMARD or TMOE_ROT_IDENTITY                       */
   int32_t ids_dtype;           /* TMOE_IDS_I32 or TMOE_IDS_I64                                 */
   int32_t block_m;             /* route-map tile rows: 8, 16, 32, 48 or 64; 0 = 16             */
+  int32_t smallm_max_tokens;   /* forwards with T <= this run as one persistent launch (the
+                                  small-M arm of flashinfer PR #69, whose default is 16); 0 = never.
+                                  Needs T*top_k <= 512 and H, I in {128, 256, 512, 1024} or not a
+                                  power of two; other calls take the five-launch path.          */
+  int32_t fc2_reduce;          /* TMOE_FC2_DETERMINISTIC (0) or TMOE_FC2_ATOMIC (1)             */
 } tmoe_config;
+
+/* FC2 reduction of the forwards: the deterministic route-major epilogue (bitwise reproducible), or
+ * the opt-in FP32-atomic sum into y ("Share trellis preparation across native and EXL3
+ * containers", b12x PR #433: optional FP32 atomic prefill reduction, which gives up bitwise
+ * summation order). */
+enum { TMOE_FC2_DETERMINISTIC = 0, TMOE_FC2_ATOMIC = 1 };
 
 typedef struct tmoe_plan_s *tmoe_plan_t;   /* opaque, host-only, immutable, shareable across threads */
 
@@ -238,6 +249,9 @@ typedef struct {                 /* where a forward call leaves its intermediate
                                     choice for T; readable after the stream completes)             */
   int32_t a1_pitch, b_pitch;     /* row pitch of a1 and b in elements: H and I for W4A8; for W4A16
                                     padded so that rows do not all start on the same memory channel */
+  int32_t *arm_status;           /* device [1]: 0 after a forward that ran as one persistent launch;
+                                    1 if a wait of that launch gave up (its y is invalid), 2 if an
+                                    earlier call on this arena failed so the launch did not run     */
 } tmoe_debug_views;
 
 /* Views of the intermediates a forward call with T tokens leaves in scratch; w4a8 names the

@@ -11,8 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(HERE, "libtmoe.so")
-SOURCES = ["k_route_map.hip", "k_rowops.hip", "k_trellis_gemm.hip", "tmoe_host.cpp"]
-HEADERS = ["tmoe_device.hpp", "tmoe_internal.hpp"]
+SOURCES = ["k_route_map.hip", "k_rowops.hip", "k_trellis_gemm.hip", "k_small_arm.hip", "tmoe_host.cpp"]
+HEADERS = ["tmoe_device.hpp", "tmoe_internal.hpp", "tmoe_rowbody.hpp", "tmoe_routemap.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

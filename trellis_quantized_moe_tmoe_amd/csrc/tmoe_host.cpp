@@ -82,7 +82,7 @@ struct Layout {
 }  // namespace
 
 struct tmoe_plan_s {
-  int H, I, E, K, max_tokens, rotation, ids64, block_m;
+  int H, I, E, K, max_tokens, rotation, ids64, block_m, smallm_max_tokens, fc2_reduce;
   std::vector<uint8_t> bits;
   std::vector<long long> offsets;   // word offset per expert, [E+1]
   uint32_t packed_bits[64];      // 4 bits per expert: its width
@@ -118,7 +118,7 @@ void build_layout(tmoe_plan_s* p) {
   L.tile_e = take(4ull * p->max_tiles);
   L.tile_r0 = take(4ull * p->max_tiles);
   L.tile_rows = take(4ull * p->max_tiles);
-  L.scalars = take(32);                               // num_tiles, status, num_gtiles, splits[2]
+  L.scalars = take(32);                               // num_tiles, status, num_gtiles, splits[2], arm status
   L.gtiles = take(16ull * p->max_gtiles);
   L.wgc = take(4ull * ((R + kRouteChunk - 1) / kRouteChunk) * (p->E + 1));   // per-workgroup route counts
   L.a1 = take(2ull * R * fp16_pitch(p->H));           // fp16 (padded rows), or E4M3 + E8M0 planes
@@ -233,10 +233,74 @@ tmoe_status check_common(const tmoe_plan_s* p, const void* ids, int T, void* scr
   return check_scratch(p, scratch, bytes);
 }
 
+// The small-batch arm runs rows of 128 to 1024 values (2 to 16 per lane) or rows rotated in
+// 128-blocks, and at most kArmMaxRoutes routes.
+bool arm_rot_ok(int n) { return !is_pow2(n) || (n >= 128 && n <= 1024); }
+bool arm_fits(const tmoe_plan_s* p, long long R) {
+  return R <= kArmMaxRoutes && arm_rot_ok(p->H) && arm_rot_ok(p->I);
+}
+
+// The whole layer as one persistent launch (k_small_arm.hip); UNSUPPORTED if it cannot run here,
+// and the caller then takes the five-launch path.
+tmoe_status forward_arm(const tmoe_plan_s* p, const void* x, const void* ids, const float* w, int32_t T,
+                        const tmoe_weights* wt, float* y, void* scratch, hipStream_t s, bool fp8) {
+  ArmSlot* slot = nullptr;
+  int groups = 0;
+  if (!small_arm_prepare(scratch, p->uniform_bits, fp8, &slot, &groups)) return TMOE_ERR_UNSUPPORTED;
+  const long long R = static_cast<long long>(T) * p->K;
+  ArmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x = static_cast<const uint16_t*>(x);
+  a.ids = ids;
+  a.ids64 = p->ids64;
+  a.w = w;
+  a.payload = wt->payload;
+  a.scale1 = wt->scale1;
+  a.scale2 = wt->scale2;
+  a.su1 = wt->su1;
+  a.sv1 = wt->sv1;
+  a.su2 = wt->su2;
+  a.sv2 = wt->sv2;
+  a.y = y;
+  a.T = T;
+  a.H = p->H;
+  a.I = p->I;
+  a.E = p->E;
+  a.K = p->K;
+  a.R = static_cast<int>(R);
+  a.rot_h = make_rot(p->H, p->rotation == TMOE_ROT_IDENTITY);
+  a.rot_i = make_rot(p->I, p->rotation == TMOE_ROT_IDENTITY);
+  a.words_per_bit = 3LL * p->H * p->I / 16;
+  a.fc2_words_per_bit = 2LL * p->H * p->I / 16;
+  const int kstep = fp8 ? 128 : 32;
+  a.s1 = choose_splits(R, p->H / kstep);
+  a.s2 = choose_splits(R, p->I / kstep);
+  a.a1 = at<uint8_t>(scratch, p->lay.a1);
+  a.a1s = a.a1 + static_cast<size_t>(R) * p->H;
+  a.lda = fp16_pitch(p->H);
+  a.z = at<float>(scratch, p->lay.z);
+  a.b = at<uint8_t>(scratch, p->lay.b);
+  a.bs = a.b + static_cast<size_t>(R) * p->I;
+  a.ldb = fp16_pitch(p->I);
+  a.v = at<float>(scratch, p->lay.v);
+  a.status = at<int32_t>(scratch, p->lay.scalars) + 1;
+  a.arm_status = at<int32_t>(scratch, p->lay.scalars) + 5;
+  a.slot = slot;
+  std::memcpy(a.packed_bits, p->packed_bits, sizeof(a.packed_bits));
+  // enough wavefronts for the widest step, and no more than are resident at once
+  const long long tiles = std::min<long long>(R, p->E + R / 16 + 1);
+  const long long units = std::max(tiles * (2 * p->I / 64) * a.s1, tiles * (p->H / 64) * a.s2);
+  const long long items = std::max(units, R + T);
+  const int need = static_cast<int>(std::min<long long>((items + 3) / 4, 1 << 20));
+  (void)hipGetLastError();
+  launch_small_arm(a, p->uniform_bits, fp8, std::max(1, std::min(groups, need)), s);
+  return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
+}
+
 // Stages: 0 route map with the input rotation, 1 FC1, 2 activation, 3 FC2, 4 combine.
 tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* w, int32_t T,
                     const tmoe_weights* wt, float* y, void* scratch, size_t bytes, void* stream, bool fp8,
-                    int first = 0, int last = 4) {
+                    int first = 0, int last = 4, bool staged = false) {
   tmoe_status st = check_common(p, ids, T, scratch, bytes);
   if (st != TMOE_OK) return st;
   if (fp8 && !p->fp8_ok) return TMOE_ERR_UNSUPPORTED;
@@ -251,6 +315,10 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const long long R = static_cast<long long>(T) * p->K;
+  if (!staged && T <= p->smallm_max_tokens && arm_fits(p, R)) {
+    const tmoe_status st_arm = forward_arm(p, x, ids, w, T, wt, y, scratch, s, fp8);
+    if (st_arm != TMOE_ERR_UNSUPPORTED) return st_arm;
+  }
   const int mg = choose_mg(R, p->E, big_cols(p, fp8));
   const int gemm_rows = tile_rows(mg);
   const GemmShape sh[2] = {gemm_shape(p, R, mg, fp8, 1), gemm_shape(p, R, mg, fp8, 2)};
@@ -531,6 +599,10 @@ tmoe_status tmoe_plan(const tmoe_config* cfg, tmoe_plan_t* out, size_t* scratch_
   p->rotation = cfg->rotation;
   p->ids64 = cfg->ids_dtype == TMOE_IDS_I64;
   p->block_m = bm ? bm : 16;
+  if (cfg->smallm_max_tokens < 0) { delete p; return TMOE_ERR_INVALID_ARG; }
+  if (cfg->fc2_reduce != TMOE_FC2_DETERMINISTIC && cfg->fc2_reduce != TMOE_FC2_ATOMIC) { delete p; return TMOE_ERR_INVALID_ARG; }
+  p->smallm_max_tokens = cfg->smallm_max_tokens;
+  p->fc2_reduce = cfg->fc2_reduce;
   p->bits.assign(cfg->expert_bits, cfg->expert_bits + p->E);
   p->offsets.assign(p->E + 1, 0);
   std::memset(p->packed_bits, 0, sizeof(p->packed_bits));
@@ -616,7 +688,7 @@ tmoe_status tmoe_forward_stages(tmoe_plan_t p, int32_t w4a8, int32_t first, int3
                                 const void* ids, const float* w, int32_t T, const tmoe_weights* wt, float* y,
                                 void* scratch, size_t bytes, void* stream) {
   if ((w4a8 != 0 && w4a8 != 1) || first < 0 || last > 4 || first > last) return TMOE_ERR_INVALID_ARG;
-  return forward(p, x, ids, w, T, wt, y, scratch, bytes, stream, w4a8 != 0, first, last);
+  return forward(p, x, ids, w, T, wt, y, scratch, bytes, stream, w4a8 != 0, first, last, true);
 }
 
 const char* tmoe_status_str(tmoe_status s) {
@@ -681,6 +753,7 @@ tmoe_status tmoe_debug_get_views(tmoe_plan_t p, int32_t T, int32_t w4a8, void* s
   out->b_scale = at<uint8_t>(scratch, p->lay.b) + static_cast<size_t>(R) * p->I;
   out->v = at<float>(scratch, p->lay.v);
   out->splits = at<int32_t>(scratch, p->lay.scalars) + 3;
+  out->arm_status = at<int32_t>(scratch, p->lay.scalars) + 5;
   out->a1_pitch = w4a8 ? p->H : fp16_pitch(p->H);
   out->b_pitch = w4a8 ? p->I : fp16_pitch(p->I);
   return TMOE_OK;

@@ -121,6 +121,44 @@ struct LinearPrepArgs {      // dense trellis linear: a = R_K(su * x_t) per toke
 // GEMM width code for experts of mixed widths that include 5 or 6 (0: mixed widths 2-4)
 constexpr int kMixedWide = 7;
 
+// The small-batch arm (one persistent launch for the whole layer): at most kArmMaxRoutes routes
+// per call; flags and counters in kArmSlots library-owned slots per GPU, one per scratch arena.
+constexpr int kArmMaxRoutes = 512;
+constexpr int kArmSlots = 64;
+struct ArmSlot;
+
+struct ArmArgs {
+  const uint16_t* x;         // bf16 [T][H]
+  const void* ids;           // [T][K]
+  int ids64;
+  const float* w;            // [T][K]
+  const uint16_t* payload;
+  const uint16_t *scale1, *scale2, *su1, *sv1, *su2, *sv2;
+  float* y;                  // [T][H]
+  int T, H, I, E, K, R;      // R = T * K
+  RowRot rot_h, rot_i;
+  long long words_per_bit;   // 3*H*I/16: payload words of one expert per bit of width
+  long long fc2_words_per_bit;   // 2*H*I/16: FC1 words per bit (FC2 starts after them)
+  int s1, s2;                // K splits of FC1 and FC2
+  uint8_t* a1;               // fp16 [R][lda] or E4M3 [R][H] (route order)
+  uint8_t* a1s;              // E8M0 [R][H/32]
+  int lda;
+  float* z;                  // [s1][R][2I] (slot order)
+  uint8_t* b;                // fp16 [R][ldb] or E4M3 [R][I] (slot order)
+  uint8_t* bs;               // E8M0 [R][I/32]
+  int ldb;
+  float* v;                  // [s2][R][H] (slot order)
+  int32_t* status;           // dropped routes
+  int32_t* arm_status;       // 0, or 1: a wait gave up in this call, 2: the slot failed earlier
+  ArmSlot* slot;
+  uint32_t packed_bits[64];  // 4 bits per expert: its width
+};
+
+// Slot of the arena and the largest co-resident grid of the arm's kernel on the current device;
+// false if the arm cannot run (no free slot, a HIP query failed).
+bool small_arm_prepare(const void* arena, int bits, bool mx, ArmSlot** slot, int* groups);
+void launch_small_arm(const ArmArgs& a, int bits, bool mx, int groups, hipStream_t s);
+
 // one workgroup for up to kRouteSingleMax routes, else a counting and a placement launch over
 // workgroups of kRouteChunk routes each
 constexpr int kRouteChunk = 1024;

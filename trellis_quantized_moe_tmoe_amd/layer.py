@@ -91,13 +91,23 @@ def device_activations(inp, device="cuda", ids_dtype=torch.int64):
 
 class Plan:
     def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int, max_tokens: int,
-                 expert_bits, rotation: str = "hadamard", ids_dtype=torch.int64, block_m: int = 0):
+                 expert_bits, rotation: str = "hadamard", ids_dtype=torch.int64, block_m: int = 0,
+                 smallm_max_tokens: int = 0, fc2_reduce: str = "deterministic"):
+        """smallm_max_tokens: forwards with at most this many tokens run as one persistent launch
+        (the pages' small-M arm, whose default is 16; here 0 = never by default, as the five-launch
+        path is faster on gfx950). fc2_reduce: "deterministic" (route-major epilogue, bitwise
+        reproducible) or "atomic" (FP32 atomic sum into y, opt-in)."""
         bits = np.ascontiguousarray(np.asarray(expert_bits, dtype=np.uint8))
         self._bits = bits
+        if fc2_reduce not in ("deterministic", "atomic"):
+            raise ValueError(f"fc2_reduce: {fc2_reduce!r}")
         self.config = native.Config(hidden, inter, num_experts, top_k, max_tokens,
                                     bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
                                     native.ROT_IDENTITY if rotation == "identity" else native.ROT_HADAMARD,
-                                    native.IDS_I64 if ids_dtype == torch.int64 else native.IDS_I32, block_m)
+                                    native.IDS_I64 if ids_dtype == torch.int64 else native.IDS_I32, block_m,
+                                    smallm_max_tokens,
+                                    native.FC2_ATOMIC if fc2_reduce == "atomic" else native.FC2_DETERMINISTIC)
+        self.smallm_max_tokens, self.fc2_reduce = smallm_max_tokens, fc2_reduce
         self.ids_dtype = ids_dtype
         handle = ctypes.c_void_p()
         sb, pw = ctypes.c_size_t(), ctypes.c_size_t()

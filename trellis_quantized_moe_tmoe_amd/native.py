@@ -16,6 +16,7 @@ STATUS_NAMES = {0: "TMOE_OK", 1: "TMOE_ERR_INVALID_ARG", 2: "TMOE_ERR_UNSUPPORTE
                 7: "TMOE_ERR_STATIC_SCRATCH"}
 STATIC_SCRATCH_BYTES = 32 << 20
 ROT_HADAMARD, ROT_IDENTITY = 0, 1
+FC2_DETERMINISTIC, FC2_ATOMIC = 0, 1
 IDS_I32, IDS_I64 = 0, 1
 
 # every symbol declared in include/tmoe.h
@@ -31,7 +32,8 @@ class Config(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
                 ("expert_bits", ctypes.POINTER(ctypes.c_uint8)), ("rotation", ctypes.c_int32),
-                ("ids_dtype", ctypes.c_int32), ("block_m", ctypes.c_int32)]
+                ("ids_dtype", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("smallm_max_tokens", ctypes.c_int32), ("fc2_reduce", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -52,7 +54,7 @@ class PlanInfo(ctypes.Structure):
 
 class DebugViews(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("a1", "a1_scale", "z", "b", "b_scale", "v", "splits")] + \
-               [("a1_pitch", ctypes.c_int32), ("b_pitch", ctypes.c_int32)]
+               [("a1_pitch", ctypes.c_int32), ("b_pitch", ctypes.c_int32), ("arm_status", ctypes.c_void_p)]
 
 
 class LinearConfig(ctypes.Structure):
