@@ -1,0 +1,107 @@
+"""The opt-in FP32-atomic FC2 reduction (plan field fc2_reduce = atomic) against the float64 oracle.
+The order of the atomic additions is not fixed, so results are compared within the W4A16 bound,
+and with each other within fp32 rounding, never bit for bit."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle_np as O
+from gpu_cases import TOL_W4A16, Case, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+class AtomicCase(Case):
+    def __init__(self, name, tokens=None, rotation="hadamard", identity_signs=False, **over):
+        super().__init__(name, tokens, rotation=rotation, identity_signs=identity_signs, **over)
+        from trellis_quantized_moe_tmoe_amd import layer as L
+        self.plan = L.Plan.for_inputs(self.inp, rotation=rotation, fc2_reduce="atomic")
+        self.det = L.Plan.for_inputs(self.inp, rotation=rotation)
+        self.scratch = self.plan.alloc_scratch()
+
+    def run_det(self):
+        y = self.det.forward(self.x, self.ids, self.w, self.weights, self.det.alloc_scratch())
+        torch.cuda.synchronize()
+        return y
+
+
+@pytest.mark.parametrize("name,T,over", [
+    ("decode", 1, {}), ("decode", 4, {}), ("decode", 16, {}),     # 16-row units, 8 / 4 K splits
+    ("prefill", 2048, {}),                                        # 128-row tiles as two 64-row units
+    ("w4a8", 64, {}),                                             # 512 routes over 256 experts
+    ("tiny", 300, dict(hidden=1024, inter=256, bits_choices=(2, 3, 4))),   # mixed widths, 128-row tiles
+    ("tiny", 100, dict(hidden=512, inter=128)),                   # rows of 512: four wavefronts
+    ("tiny", 20, dict(hidden=1024, inter=128, experts=4, top_k=1)),         # 32-row units
+])
+def test_fc2_atomic_w4a16(name, T, over):
+    c = AtomicCase(name, T, **over)
+    y = c.run().cpu().numpy()
+    err = rel_err(y, c.oracle_w4a16)
+    d = rel_err(y, c.run_det().cpu().numpy())
+    say(f"[result] {c.label} atomic FC2 rel err {err:.3e} (vs deterministic path {d:.3e})")
+    assert err <= TOL_W4A16
+    assert d <= 1e-4
+
+
+def test_fc2_atomic_identity_mode():
+    c = AtomicCase("tiny", 64, hidden=1024, inter=128, rotation="identity", identity_signs=True)
+    assert rel_err(c.run().cpu().numpy(), c.oracle_w4a16) <= TOL_W4A16
+
+
+def test_fc2_atomic_dropped_routes_and_an_empty_token():
+    c = AtomicCase("decode", 16)
+    ids = c.inp.ids.copy()
+    ids[0, 2] = -1
+    ids[5, :] = 96
+    c.ids = torch.from_numpy(ids).cuda()
+    y = c.run().cpu().numpy()
+    w = c.inp.weights.copy()
+    w[0, 2] = 0.0
+    w[5, :] = 0.0
+    fixed = ids.copy()
+    fixed[0, 2] = 0
+    fixed[5, :] = np.arange(8)
+    ref = O.forward(dataclasses.replace(c.inp, ids=fixed, weights=w))
+    assert np.all(y[5] == 0.0)
+    assert rel_err(y, ref) <= TOL_W4A16
+
+
+def test_fc2_atomic_graph_replays_zero_y_each_time():
+    from trellis_quantized_moe_tmoe_amd.workloads import make_inputs
+    c = AtomicCase("decode", 16)
+    y = torch.empty((16, c.inp.hidden), device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c.plan.forward(c.x, c.ids, c.w, c.weights, c.scratch, y=y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        c.plan.forward(c.x, c.ids, c.w, c.weights, c.scratch, y=y)
+    for seed in (31, 32):
+        other = make_inputs("decode", tokens=16, seed=seed)
+        c.x.copy_(torch.from_numpy(other.x_bf16.view(np.int16)).cuda())
+        c.ids.copy_(torch.from_numpy(other.ids).cuda())
+        c.w.copy_(torch.from_numpy(other.weights).cuda())
+        ref = O.forward(dataclasses.replace(c.inp, x_bf16=other.x_bf16, ids=other.ids, weights=other.weights))
+        for _ in range(3):                    # y is zeroed inside each replay: no accumulation across replays
+            g.replay()
+            torch.cuda.synchronize()
+            eager = c.plan.forward(c.x, c.ids, c.w, c.weights, c.scratch).clone()
+            torch.cuda.synchronize()
+            assert rel_err(y.cpu().numpy(), eager.cpu().numpy()) <= 1e-5
+            assert rel_err(y.cpu().numpy(), ref) <= TOL_W4A16
+
+
+def test_fc2_atomic_falls_back_where_it_does_not_apply():
+    # rows of 256 values (and W4A8) keep the deterministic epilogue: bit-identical to the default plan
+    c = AtomicCase("tiny", 4)
+    assert torch.equal(c.run(), c.run_det())
+    c8 = AtomicCase("w4a8", 8)
+    y8 = c8.run(w4a8=True)
+    from trellis_quantized_moe_tmoe_amd import layer as L
+    y8d = c8.det.forward(c8.x, c8.ids, c8.w, c8.weights, c8.det.alloc_scratch(), w4a8=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y8, y8d)

@@ -194,6 +194,15 @@ struct ActBody {
 // inside one segment of the intermediate row.
 template <int EPL, bool MX, int SMAX>
 __global__ __launch_bounds__(256) void k_act(ActArgs a) {
+  if (static_cast<int>(blockIdx.x) >= a.act_blocks) {      // zero y for the atomic FC2 reduction
+    const long long i0 = (static_cast<long long>(blockIdx.x) - a.act_blocks) * 256 * 4 + 4 * threadIdx.x;
+    if (i0 + 3 < a.y_count) {
+      *reinterpret_cast<float4*>(a.y_zero + i0) = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      for (long long i = i0; i < a.y_count; ++i) a.y_zero[i] = 0.0f;
+    }
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int nseg = EPL > 0 ? 1 : row_segments(a.rot);
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -580,8 +589,11 @@ int combine_waves(int hidden, int top_k) {
 
 }  // namespace
 
-void launch_act(const ActArgs& a, bool mx, hipStream_t s) {
-  const unsigned grid = blocks_for(static_cast<long long>(a.routes) * row_segments(a.rot));
+void launch_act(const ActArgs& a_in, bool mx, hipStream_t s) {
+  ActArgs a = a_in;
+  a.act_blocks = static_cast<int>(blocks_for(static_cast<long long>(a.routes) * row_segments(a.rot)));
+  const long long zero_blocks = a.y_zero ? (a.y_count + 1023) / 1024 : 0;
+  const unsigned grid = static_cast<unsigned>(a.act_blocks + zero_blocks);
   dispatch_epl(a.rot, [&](auto epl) {
     dispatch_smax(a.nsplit, [&](auto sm) {
       constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;

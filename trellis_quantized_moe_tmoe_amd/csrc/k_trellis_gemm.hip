@@ -558,6 +558,179 @@ __global__ __launch_bounds__(256) void k_gemm_f8(GemmArgs a) {
   }
 }
 
+// FC2 with the opt-in FP32-atomic reduction ("Share trellis preparation across native and EXL3
+// containers", b12x PR #433: the optional FP32 atomic prefill reduction, which gives up a bitwise
+// summation order). A workgroup of NW = H/128 wavefronts owns whole output rows: its unit is (GEMM
+// tile, block of 16*MG rows of it, K split), and wavefront wv computes columns [128 wv, 128 wv +
+// 128) of the block (8 strips, decoded by that wavefront alone, once per block). The epilogue goes
+// one 16-row group at a time through LDS as fp32 rows; a wavefront then takes whole rows and applies
+// the combine's per-route work -- scale2, the H-point rotation, sv2, the route's top-k weight -- and
+// adds the row into y[t] with fp32 atomics. The split-plane v and the combine launch disappear; the
+// sum over a token's routes and over the K splits (each split's partial is rotated and added on
+// its own: every step after the contraction is linear) follows the order in which the atomics land.
+constexpr int FNS = 8;   // 16-column strips per wavefront (128 columns)
+
+template <int BITS, int MG>
+constexpr int fa_ring_words() { return DF * (2 * FNS * 8 * 4 + MG * 256); }
+
+template <int BITS, int MG, int NW>
+__device__ __forceinline__ void fc2_atomic_unit(const Fc2AtomicArgs& fa, const int4 t, int row0, int rows, int s,
+                                                int splits, int lane, int wv, uint32_t* lds_all, uint32_t mask,
+                                                uint32_t orv) {
+  const GemmArgs& a = fa.g;
+  constexpr int TW = 8 * BITS;
+  constexpr int BW = 2 * FNS * TW;                     // trellis words per K step
+  constexpr int AOFF = 2 * FNS * 8 * 4;                // A fragments after the trellis words (sized for 4 bits)
+  constexpr int STAGE = AOFF + MG * 256;
+  constexpr int CPT = TW / 4;
+  constexpr int NL = BW / 4 > 64 ? 2 : 1;
+  static_assert(BW / 4 <= 128, "two staging loads per step at most");
+  constexpr int H = 128 * NW;
+  uint32_t* ring = lds_all + wv * fa_ring_words<BITS, MG>();
+  const long long woff = (static_cast<long long>(static_cast<unsigned>(t.w)) << 8);
+  const int NT = H >> 4;
+  const int col = lane & 15, grp = lane >> 4;
+  const int q = 2 * col + (grp & 1);
+  const int ksteps = (a.K >> 5) / splits;
+  const int ks0 = s * ksteps, ks1 = ks0 + ksteps;
+  const int nt0 = wv * FNS;
+  const gptr<uint32_t> mat = uniform_ptr(reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS) +
+                                         static_cast<size_t>(nt0) * TW);
+  const gptr<_Float16> A = uniform_ptr(static_cast<const _Float16*>(a.a));
+  const bool stager = lane < BW / 4;
+  const int st_off = ((lane / (FNS * CPT)) * NT + (lane / CPT) % FNS) * TW + 4 * (lane % CPT);
+  const int c2 = 64 + lane;
+  const bool stager2 = NL == 2 && c2 < BW / 4;
+  const int st2_off = ((c2 / (FNS * CPT)) * NT + (c2 / CPT) % FNS) * TW + 4 * (c2 % CPT);
+  const int kstride = 2 * NT * TW;
+  const int j0 = window_word<BITS>(q);
+  const int rd_a = (grp >> 1) * FNS * TW + (j0 < 0 ? j0 + TW : j0);
+  const int rd_b = (grp >> 1) * FNS * TW + ((j0 + 1 == TW) ? 0 : j0 + 1);
+  long long aoff[MG];
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg) aoff[mg] = static_cast<long long>(row0 + min(16 * mg + col, rows - 1)) * a.lda + 8 * grp;
+  const bool a_live = col < rows;
+
+  f4 acc[MG][FNS];
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+    for (int ns = 0; ns < FNS; ++ns) acc[mg][ns] = f4{0.f, 0.f, 0.f, 0.f};
+
+  auto issue = [&](int ks, int d) {
+    uint32_t* slot = ring + d * STAGE;
+    if (stager)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(mat + static_cast<size_t>(ks) * kstride + st_off),
+                                       (void __attribute__((address_space(3)))*)(slot), 16, 0, 0);
+    if constexpr (NL == 2) {
+      if (stager2)
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(mat + static_cast<size_t>(ks) * kstride + st2_off),
+                                         (void __attribute__((address_space(3)))*)(slot + 256), 16, 0, 0);
+    }
+    const gptr<_Float16> ab = A + 32 * ks;
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg)
+      if (mg > 0 || a_live)
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(ab + aoff[mg]),
+                                         (void __attribute__((address_space(3)))*)(slot + AOFF + mg * 256), 16, 0, 0);
+  };
+  auto step = [&](int d, int next) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DF - 1) * (NL + MG)) : "memory");
+    const uint32_t* slot = ring + d * STAGE;
+    uint32_t wh[FNS], wl[FNS];
+#pragma unroll
+    for (int ns = 0; ns < FNS; ++ns) {
+      wh[ns] = slot[rd_a + ns * TW];
+      wl[ns] = slot[rd_b + ns * TW];
+    }
+    half8 aa[MG];
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) aa[mg] = *reinterpret_cast<const half8*>(slot + AOFF + mg * 256 + 4 * lane);
+    half8 b[FNS];
+#pragma unroll
+    for (int ns = 0; ns < FNS; ++ns) b[ns] = decode8<BITS>(wh[ns], wl[ns], q, mask, orv);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue(next, d);
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+      for (int ns = 0; ns < FNS; ++ns)
+        acc[mg][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aa[mg], b[ns], acc[mg][ns], 0, 0, 0);
+  };
+#pragma unroll
+  for (int d = 0; d < DF; ++d) issue(min(ks0 + d, ks1 - 1), d);
+  int base = ks0;
+  for (; base + DF <= ks1; base += DF) {
+#pragma unroll
+    for (int d = 0; d < DF; ++d) step(d, min(base + d + DF, ks1 - 1));
+  }
+#pragma unroll
+  for (int d = 0; d < DF; ++d)
+    if (base + d < ks1) step(d, ks1 - 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();                                   // every ring is idle: LDS becomes the row buffer
+
+  float* rowbuf = reinterpret_cast<float*>(lds_all);  // [16][H]
+  const int e = t.x & 0xffffff;
+  const uint16_t* c2v = fa.scale2 + static_cast<size_t>(e) * H + lane;
+  const uint16_t* sgv = fa.sv2 + static_cast<size_t>(e) * H + lane;
+  constexpr int S = H / 64;
+#pragma unroll
+  for (int g = 0; g < MG; ++g) {
+    if (16 * g >= rows) break;                        // uniform over the workgroup
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int ns = 0; ns < FNS; ++ns) rowbuf[(4 * grp + i) * H + 128 * wv + 16 * ns + col] = acc[g][ns][i];
+    __syncthreads();
+    const int nrows = min(16, rows - 16 * g);
+    for (int rr = wv; rr < nrows; rr += NW) {
+      const int p = row0 + 16 * g + rr;
+      const int route = fa.sorted_routes[p];
+      const float wt = fa.w[route];
+      float v[S];
+#pragma unroll
+      for (int i = 0; i < S; ++i) v[i] = rowbuf[rr * H + 64 * i + lane] * h2f(c2v[64 * i]);
+      if (!fa.identity) fwht_segment<S>(v, lane);
+      float* yr = fa.y + static_cast<size_t>(route / fa.top_k) * H + lane;
+#pragma unroll
+      for (int i = 0; i < S; ++i)
+        __hip_atomic_fetch_add(yr + 64 * i, wt * (v[i] * h2f(sgv[64 * i])), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();                                  // the row buffer is rewritten next
+  }
+}
+
+template <int BITS, int MG, int NW>
+__global__ __launch_bounds__(64 * NW) void k_fc2_atomic(Fc2AtomicArgs fa) {
+  constexpr int RING = NW * fa_ring_words<BITS, MG>();
+  constexpr int ROWS = 16 * 128 * NW;                // one 16-row group of fp32 rows
+  __shared__ uint32_t lds_all[RING > ROWS ? RING : ROWS];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int splits = fa.g.nsplit;
+  const int subs = fa.tile_rows / fa.sub_rows;
+  const int units = *fa.g.num_gtiles * subs * splits;
+  const uint32_t mask = vreg_const(kMcgMask), orv = kMcgOr;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int s = u % splits;
+    const int rest = u / splits;
+    const int sub = rest % subs;
+    const int4 t = fa.g.gtiles[rest / subs];
+    const int rows = min(fa.sub_rows, t.z - sub * fa.sub_rows);
+    if (rows <= 0) continue;                          // uniform: a part of a tile past its last row
+    const int row0 = t.y + sub * fa.sub_rows;
+    if constexpr (BITS != 0) {
+      fc2_atomic_unit<BITS, MG, NW>(fa, t, row0, rows, s, splits, lane, wv, lds_all, mask, orv);
+    } else {
+      const int bits = (t.x >> 24) & 0xff;
+      if (bits == 4) fc2_atomic_unit<4, MG, NW>(fa, t, row0, rows, s, splits, lane, wv, lds_all, mask, orv);
+      else if (bits == 3) fc2_atomic_unit<3, MG, NW>(fa, t, row0, rows, s, splits, lane, wv, lds_all, mask, orv);
+      else fc2_atomic_unit<2, MG, NW>(fa, t, row0, rows, s, splits, lane, wv, lds_all, mask, orv);
+    }
+  }
+}
+
 // Dense decode of one K x N matrix with the GEMM's own lane mapping and decode (test hook).
 template <int BITS>
 __global__ __launch_bounds__(256) void k_debug_decode(const uint16_t* words, int K, int N, int as_e4m3,
@@ -662,6 +835,28 @@ void launch_gemm_f8(const GemmArgs& a, int fc, int bits, int mg, int waves, hipS
   const dim3 grid((waves + 3) / 4);
   if (fc == 1) launch_f8_bits<1>(a, bits, mg, grid, s);
   else launch_f8_bits<2>(a, bits, mg, grid, s);
+}
+
+void launch_fc2_atomic(const Fc2AtomicArgs& a, int bits, int mg2, int groups, hipStream_t s) {
+  auto go = [&](auto b_c, auto m_c, auto w_c) {
+    constexpr int B = decltype(b_c)::value, M = decltype(m_c)::value, NW = decltype(w_c)::value;
+    hipLaunchKernelGGL((k_fc2_atomic<B, M, NW>), dim3(groups), dim3(64 * NW), 0, s, a);
+  };
+  auto with_mg = [&](auto b_c, auto w_c) {
+    if (mg2 >= 4) go(b_c, std::integral_constant<int, 4>{}, w_c);
+    else if (mg2 == 2) go(b_c, std::integral_constant<int, 2>{}, w_c);
+    else go(b_c, std::integral_constant<int, 1>{}, w_c);
+  };
+  auto with_bits = [&](auto w_c) {
+    switch (bits) {
+      case 4: with_mg(std::integral_constant<int, 4>{}, w_c); break;
+      case 3: with_mg(std::integral_constant<int, 3>{}, w_c); break;
+      case 2: with_mg(std::integral_constant<int, 2>{}, w_c); break;
+      default: with_mg(std::integral_constant<int, 0>{}, w_c); break;
+    }
+  };
+  if (a.g.N == 1024) with_bits(std::integral_constant<int, 8>{});
+  else with_bits(std::integral_constant<int, 4>{});
 }
 
 void launch_debug_decode(const uint16_t* matrix_words, int bits, int K, int N, int as_e4m3, void* out,

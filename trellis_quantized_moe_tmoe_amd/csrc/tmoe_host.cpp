@@ -233,6 +233,12 @@ tmoe_status check_common(const tmoe_plan_s* p, const void* ids, int T, void* scr
   return check_scratch(p, scratch, bytes);
 }
 
+// The FP32-atomic FC2 reduction: W4A16, widths 2-4, output rows of 512 or 1024 values (one
+// workgroup of H/128 wavefronts owns whole rows); other plans keep the deterministic epilogue.
+bool fc2_atomic_fits(const tmoe_plan_s* p, bool fp8) {
+  return !fp8 && p->max_bits <= 4 && (p->H == 512 || p->H == 1024);
+}
+
 // The small-batch arm runs rows of 128 to 1024 values (2 to 16 per lane) or rows rotated in
 // 128-blocks, and at most kArmMaxRoutes routes.
 bool arm_rot_ok(int n) { return !is_pow2(n) || (n >= 128 && n <= 1024); }
@@ -385,6 +391,11 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   aa.b_scale = bs;
   aa.ldb = fp16_pitch(p->I);
   aa.routes = static_cast<int>(R);
+  // the FP32-atomic FC2 reduction adds into y, which the activation launch zeroes beforehand
+  const bool atomic_fc2 = p->fc2_reduce == TMOE_FC2_ATOMIC && fc2_atomic_fits(p, fp8);
+  aa.y_zero = atomic_fc2 ? y : nullptr;
+  aa.y_count = atomic_fc2 ? static_cast<long long>(T) * p->H : 0;
+  aa.act_blocks = 0;
   if (on(2)) launch_act(aa, fp8, s);
 
   GemmArgs g2 = g1;
@@ -398,7 +409,25 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g2.nsplit = sh[1].most;
   g2.arow = nullptr;
   const int waves2 = sh[1].waves;
-  if (on(3)) {
+  if (on(3) && atomic_fc2) {
+    Fc2AtomicArgs fa;
+    fa.g = g2;
+    fa.sorted_routes = sorted;
+    fa.ids = ids;
+    fa.ids64 = p->ids64;
+    fa.w = w;
+    fa.scale2 = wt->scale2;
+    fa.sv2 = wt->sv2;
+    fa.identity = p->rotation == TMOE_ROT_IDENTITY;
+    fa.top_k = p->K;
+    fa.tile_rows = gemm_rows;
+    const int mg2 = std::min(mg, 4);
+    fa.sub_rows = 16 * mg2;
+    fa.y = y;
+    const long long gt_ub = std::min<long long>(R, p->E + R / gemm_rows + 1);
+    const long long units = gt_ub * (gemm_rows / fa.sub_rows) * sh[1].most;
+    launch_fc2_atomic(fa, p->uniform_bits, mg2, static_cast<int>(std::min<long long>(units, 2048)), s);
+  } else if (on(3)) {
     if (fp8) launch_gemm_f8(g2, 2, p->uniform_bits, mg, waves2, s);
     else launch_gemm_f16(g2, 2, p->uniform_bits, mg, waves2, s);
   }
@@ -420,7 +449,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   // non-power-of-two rows: few tokens (token x block items up to 2048) get a workgroup per (token,
   // block) with one wavefront per route; more tokens a wavefront per (token, block) for all routes
   ca.split_segments = static_cast<long long>(T) * make_rot(p->H, 0).nblk128 <= 2048 ? 1 : 0;
-  if (on(4)) launch_combine(ca, s);
+  if (on(4) && !atomic_fc2) launch_combine(ca, s);
 
   return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
 }

@@ -71,6 +71,9 @@ struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_
   uint8_t* b_scale;          // [R][I/32]
   int ldb;                   // fp16 row pitch in elements (>= I)
   int routes;
+  float* y_zero;             // non-null: workgroups past the activation's also zero y (the atomic
+  long long y_count;         //   FC2 reduction adds into it); y_count floats
+  int act_blocks;            // workgroups of the activation itself
 };
 
 struct CombineArgs {         // y_t = sum_j w[t,j] * sv2_e * R_H(scale2_e * v_slot), j ascending
@@ -104,6 +107,21 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
   int K, N;
   int lda;                   // fp16 A row pitch in elements (the fp8 kernels use K)
   int routes;                // R: row stride between split planes
+};
+
+struct Fc2AtomicArgs {        // y_t += w[t,j] * sv2_e * R_H(scale2_e * (C2_e^T b_slot)), added atomically
+  GemmArgs g;                // FC2 operands: b rows by slot, the GEMM tile list, K = I, N = H (out unused)
+  const int32_t* sorted_routes;   // slot -> route
+  const void* ids;
+  int ids64;
+  const float* w;            // [T][k]
+  const uint16_t* scale2;    // [E][H]
+  const uint16_t* sv2;       // [E][H]
+  int identity;              // rotation off (test mode)
+  int top_k;
+  int tile_rows;             // rows of a GEMM tile (16 * mg)
+  int sub_rows;              // rows of one unit: 16 * MG (MG = 1, 2 or 4 row groups)
+  float* y;                  // [T][H], zeroed earlier in the forward
 };
 
 struct LinearPrepArgs {      // dense trellis linear: a = R_K(su * x_t) per token, plus the tables the
@@ -172,6 +190,9 @@ void launch_combine(const CombineArgs& a, hipStream_t s);
 // mg: 16-row groups per GEMM tile (1, 2 or 4); waves: persistent wave count
 void launch_gemm_f16(const GemmArgs& a, int fc, int bits, int mg, int waves, hipStream_t s);
 void launch_gemm_f8(const GemmArgs& a, int fc, int bits, int mg, int waves, hipStream_t s);
+// FC2 with the FP32-atomic reduction into y (H = 512 or 1024): workgroups of H/128 wavefronts,
+// `groups` of them persistent over the (tile, row block, K split) units; mg2 = 16-row groups per unit.
+void launch_fc2_atomic(const Fc2AtomicArgs& a, int bits, int mg2, int groups, hipStream_t s);
 
 void launch_debug_decode(const uint16_t* matrix_words, int bits, int K, int N, int as_e4m3, void* out,
                          hipStream_t s);
