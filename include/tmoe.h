@@ -241,10 +241,14 @@ typedef struct {                 /* where a forward call leaves its intermediate
                                     (row t*k + j); the first H entries of each row are the rotated
                                     input                                                          */
   uint8_t *a1_scale;             /* [T*k][H/32] E8M0 (W4A8), route order                         */
-  float *z;                      /* [splits[0]][T*k][2I] fp32 FC1 partial sums, unscaled, slot order */
+  float *z;                      /* [splits[0]][T*k][2I] fp32 FC1 partial sums, unscaled, slot order;
+                                    where half_planes[0] is 1 instead one fp16 plane [T*k][2I] of
+                                    the finished sums times scale1                                  */
   void *b;                       /* [T*k][b_pitch] fp16 or E4M3, slot order (first I entries used) */
   uint8_t *b_scale;              /* [T*k][I/32] E8M0 (W4A8)                                      */
-  float *v;                      /* [splits[1]][T*k][H] fp32 FC2 partial sums, unscaled, slot order */
+  float *v;                      /* [splits[1]][T*k][H] fp32 FC2 partial sums, unscaled, slot order;
+                                    where half_planes[1] is 1 instead one fp16 plane [T*k][H] of
+                                    the finished sums times scale2                                  */
   int32_t *splits;               /* device [2]: K splits of FC1 and FC2 that the call used (the plan's
                                     choice for T; readable after the stream completes)             */
   int32_t a1_pitch, b_pitch;     /* row pitch of a1 and b in elements: H and I for W4A8; for W4A16
@@ -252,6 +256,8 @@ typedef struct {                 /* where a forward call leaves its intermediate
   int32_t *arm_status;           /* device [1]: 0 after a forward that ran as one persistent launch;
                                     1 if a wait of that launch gave up (its y is invalid), 2 if an
                                     earlier call on this arena failed so the launch did not run     */
+  int32_t *half_planes;          /* device [2]: 1 where FC1 (FC2) left the fp16 plane described at z
+                                    (v): calls with one K split on 128-row tiles                   */
 } tmoe_debug_views;
 
 /* Views of the intermediates a forward call with T tokens leaves in scratch; w4a8 names the

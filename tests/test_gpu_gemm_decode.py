@@ -8,7 +8,9 @@ fp16 codes (W4A16) or with their E4M3 roundings (W4A8: the one-hot operand is th
 with the block scale 2^-8, so the product is exactly the weight operand). This grades the decode
 as the GEMM kernels perform it -- their LDS-ring offsets, the second staging load of widths 5 and
 6, the E4M3 lane mapping -- on every tile shape: 16-, 32- and 64-row wavefront tiles, 128-row
-workgroup tiles of 128 and 256 columns, and the scaled-fp8 kernel."""
+workgroup tiles of 128 and 256 columns, and the scaled-fp8 kernel. The channel scales are set to 1:
+where a GEMM finishes its sums in one launch it applies the scale and rounds to fp16, which then
+returns the code itself."""
 import numpy as np
 import pytest
 import torch
@@ -38,8 +40,11 @@ class Probe:
         self.sorted = rm["sorted_routes"][: self.valid]
         self.flat_ids = inp.ids.reshape(-1)
         self.codes = {}
+        self.halves = 0
         self.lut = e4m3_of_fp16_table() if w4a8 else None
         self.y = torch.empty((inp.tokens, inp.hidden), dtype=torch.float32, device="cuda")
+        case.weights.scale1.fill_(1.0)
+        case.weights.scale2.fill_(1.0)
 
     def expert(self, e):
         if e not in self.codes:
@@ -92,9 +97,16 @@ class Probe:
             self.stage(3, 3)
         torch.cuda.synchronize()
         splits = scratch_view(c.scratch, v.splits, (2,), torch.int32).cpu().numpy()
+        half = scratch_view(c.scratch, v.half_planes, (2,), torch.int32).cpu().numpy()
         S = int(splits[matrix])
-        out = scratch_view(c.scratch, v.z if matrix == 0 else v.v, (S, R, N), torch.float32)
-        got = out.double().sum(0).cpu().numpy()
+        if half[matrix]:                                # one fp16 plane, times the channel scale 1
+            assert S == 1
+            out = scratch_view(c.scratch, v.z if matrix == 0 else v.v, (R, N), torch.float16)
+            got = out.double().cpu().numpy()
+        else:
+            out = scratch_view(c.scratch, v.z if matrix == 0 else v.v, (S, R, N), torch.float32)
+            got = out.double().sum(0).cpu().numpy()
+        self.halves += int(half[matrix])
         for p in range(self.valid):
             r = int(self.sorted[p])
             e = int(self.flat_ids[r])
@@ -142,4 +154,5 @@ def test_gemm_decode_bit_exact(name, T, over, w4a8):
     for matrix in (0, 1):
         for salt in (0, 1):
             n += pr.check(matrix, salt)
-    say(f"[result] {c.label} {'W4A8' if w4a8 else 'W4A16'} in-GEMM decode: {n} one-hot rows bit-exact")
+    say(f"[result] {c.label} {'W4A8' if w4a8 else 'W4A16'} in-GEMM decode: {n} one-hot rows bit-exact "
+        f"({pr.halves} of 4 checks on fp16 planes)")

@@ -139,6 +139,10 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
     *a.num_gtiles = totals.z;
     a.splits[0] = a.nsplit[0];
     a.splits[1] = a.nsplit[1];
+    if (a.half) {
+      a.half[0] = a.nhalf[0];
+      a.half[1] = a.nhalf[1];
+    }
     *a.status = bad;
   }
   // slots past the filled ones (dropped routes leave them empty) read as expert -1

@@ -12,6 +12,8 @@
 //
 // The FC1/FC2 GEMMs leave up to 8 K-split partial planes; every reader sums them in ascending split
 // order, with all loads of a row issued before the first add so one memory latency covers them.
+// With one K split the 128-row-tile GEMMs instead leave one fp16 plane with the channel scale
+// already applied; the readers take it as template split count SMAX = 0.
 #include "tmoe_device.hpp"
 #include "tmoe_internal.hpp"
 #include "tmoe_rowbody.hpp"
@@ -94,6 +96,21 @@ __device__ __forceinline__ void sum_splits_blocked(const float* __restrict__ src
   }
 }
 
+// out[i] = scale[64 i] * (sum of the split planes at src[64 i]), or with SMAX = 0 the fp16 plane's
+// value h[64 i], which holds that product already (src, h and scale at the lane's first value).
+template <int S, int SMAX, int SU>
+__device__ __forceinline__ void scaled_values(const float* __restrict__ src, const uint16_t* __restrict__ h,
+                                              size_t plane, int splits, const uint16_t* scale, float (&out)[S]) {
+  if constexpr (SMAX == 0) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) out[i] = h2f(h[64 * i]);
+  } else {
+    sum_splits<S, SMAX, SU>(src, plane, splits, out);
+#pragma unroll
+    for (int i = 0; i < S; ++i) out[i] *= h2f(scale[64 * i]);
+  }
+}
+
 __device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 template <bool MX, int SMAX>
@@ -110,16 +127,11 @@ struct ActBody {
     }
     float zg[S], zu[S];
     const size_t plane = static_cast<size_t>(a.routes) * 2 * I;
-    const float* zr = a.z + static_cast<size_t>(p) * 2 * I + off + lane;
-    constexpr int SU = splits_unroll<S, SMAX>(2);
-    sum_splits<S, SMAX, SU>(zr, plane, splits, zg);
-    sum_splits<S, SMAX, SU>(zr + I, plane, splits, zu);
+    const size_t zo = static_cast<size_t>(p) * 2 * I + off + lane;
     const uint16_t* c1 = a.scale1 + static_cast<size_t>(e) * 2 * I + off + lane;
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-      zg[i] *= h2f(c1[64 * i]);
-      zu[i] *= h2f(c1[I + 64 * i]);
-    }
+    constexpr int SU = SMAX > 0 ? splits_unroll<S, SMAX>(2) : 1;
+    scaled_values<S, SMAX, SU>(a.z + zo, a.z16 + zo, plane, splits, c1, zg);
+    scaled_values<S, SMAX, SU>(a.z + zo + I, a.z16 + zo + I, plane, splits, c1 + I, zu);
     if (!a.rot.identity) {
       fwht_segment<S>(zg, lane);
       fwht_segment<S>(zu, lane);
@@ -149,21 +161,28 @@ struct ActBody {
   template <int S>
   __device__ __forceinline__ void run_blocked(int off) {
     const size_t plane = static_cast<size_t>(a.routes) * 2 * I;
-    const float* zr = a.z + static_cast<size_t>(p) * 2 * I + off + S * lane;
-    float zg[S], zu[S];
-    sum_splits_blocked<S, SMAX, splits_unroll<S, SMAX>(2)>(zr, plane, zg);
-    sum_splits_blocked<S, SMAX, splits_unroll<S, SMAX>(2)>(zr + I, plane, zu);
+    const size_t zo = static_cast<size_t>(p) * 2 * I + off + S * lane;
     const size_t erow = static_cast<size_t>(e) * 2 * I + off + S * lane;
-    float cg[S], cu[S], sg[S], su[S], s2[S];
-    load_f16_blocked<S>(a.scale1 + erow, cg);
-    load_f16_blocked<S>(a.scale1 + erow + I, cu);
+    float zg[S], zu[S], sg[S], su[S], s2[S];
+    if constexpr (SMAX == 0) {                 // one fp16 plane, scale1 applied
+      load_f16_blocked<S>(a.z16 + zo, zg);
+      load_f16_blocked<S>(a.z16 + zo + I, zu);
+    } else {
+      sum_splits_blocked<S, SMAX, splits_unroll<S, SMAX>(2)>(a.z + zo, plane, zg);
+      sum_splits_blocked<S, SMAX, splits_unroll<S, SMAX>(2)>(a.z + zo + I, plane, zu);
+    }
     load_f16_blocked<S>(a.sv1 + erow, sg);
     load_f16_blocked<S>(a.sv1 + erow + I, su);
     load_f16_blocked<S>(a.su2 + static_cast<size_t>(e) * I + off + S * lane, s2);
+    if constexpr (SMAX > 0) {
+      float cg[S], cu[S];
+      load_f16_blocked<S>(a.scale1 + erow, cg);
+      load_f16_blocked<S>(a.scale1 + erow + I, cu);
 #pragma unroll
-    for (int i = 0; i < S; ++i) {
-      zg[i] *= cg[i];
-      zu[i] *= cu[i];
+      for (int i = 0; i < S; ++i) {
+        zg[i] *= cg[i];
+        zu[i] *= cu[i];
+      }
     }
     if (!a.rot.identity) {
       fwht_segment<S>(zg, lane);
@@ -272,11 +291,10 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
         constexpr int S = decltype(s_const)::value;
         const float wt = w_r;
         float vv[S];
-        sum_splits<S, SMAX, splits_unroll<S, SMAX>(1)>(a.v + static_cast<size_t>(p) * H + off + lane, plane, splits, vv);
+        const size_t vo = static_cast<size_t>(p) * H + off + lane;
         const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + off + lane;
         const uint16_t* sg = a.sv2 + static_cast<size_t>(e) * H + off + lane;
-#pragma unroll
-        for (int i = 0; i < S; ++i) vv[i] *= h2f(c2[64 * i]);
+        scaled_values<S, SMAX, (SMAX > 0 ? splits_unroll<S, SMAX>(1) : 1)>(a.v + vo, a.v16 + vo, plane, splits, c2, vv);
         if (!a.rot.identity) fwht_segment<S>(vv, lane);
 #pragma unroll
         for (int i = 0; i < S; ++i) row[64 * i + lane] = wt * (vv[i] * h2f(sg[64 * i]));
@@ -287,7 +305,7 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
       } else if constexpr (EPL <= 16) {
         in_registers(std::integral_constant<int, EPL>{});
       } else {
-        const float* src = a.v + static_cast<size_t>(p) * H + lane;
+        const size_t vo = static_cast<size_t>(p) * H + lane;
         const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * H + lane;
         constexpr int U = 8;
         // (here EPL >= 32: the row is one block of 64 * EPL values, a multiple of 512); unrolled,
@@ -295,9 +313,10 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
 #pragma unroll
         for (int base = 0; base < 64 * EPL; base += 64 * U) {
           float sum[U];
-          sum_splits<U, SMAX, splits_unroll<U, SMAX>(1)>(src + base, plane, splits, sum);
+          scaled_values<U, SMAX, (SMAX > 0 ? splits_unroll<U, SMAX>(1) : 1)>(a.v + vo + base, a.v16 + vo + base, plane,
+                                                                          splits, c2 + base, sum);
 #pragma unroll
-          for (int i = 0; i < U; ++i) row[base + 64 * i + lane] = sum[i] * h2f(c2[base + 64 * i]);
+          for (int i = 0; i < U; ++i) row[base + 64 * i + lane] = sum[i];
         }
         CombineRotBody body{a, row, lane, e, w_r};
         for_segments<EPL>(a.rot, body);
@@ -334,7 +353,7 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
 template <int S, int SMAX>
 __device__ __forceinline__ void combine_block(const CombineArgs& a, int t, int off, int lane) {
 #pragma clang fp contract(off)
-  constexpr int JB = 16 / SMAX;
+  constexpr int JB = SMAX > 0 ? 16 / SMAX : 16;
   const int H = a.rot.n, K = a.top_k;         // K <= 32
   const size_t plane = static_cast<size_t>(a.routes) * H;
   const int rl = t * K + (lane < K ? lane : K - 1);
@@ -354,21 +373,28 @@ __device__ __forceinline__ void combine_block(const CombineArgs& a, int t, int o
       p[jb] = j0 + jb < K ? __builtin_amdgcn_readlane(p_l, j) : -1;
       const int e = p[jb] >= 0 ? __builtin_amdgcn_readlane(e_l, j) : 0;   // a dropped route's id may be invalid
       const int pp = p[jb] >= 0 ? p[jb] : 0;
-      sum_splits<S, SMAX, SMAX>(a.v + static_cast<size_t>(pp) * H + off + lane, plane, SMAX, vv[jb]);
+      const size_t vo = static_cast<size_t>(pp) * H + off + lane;
       const uint16_t* cs = a.scale2 + static_cast<size_t>(e) * H + off + lane;
       const uint16_t* ss = a.sv2 + static_cast<size_t>(e) * H + off + lane;
+      if constexpr (SMAX == 0) {               // one fp16 plane, scale2 applied
 #pragma unroll
-      for (int i = 0; i < S; ++i) {
-        c2[jb][i] = h2f(cs[64 * i]);
-        sg[jb][i] = h2f(ss[64 * i]);
+        for (int i = 0; i < S; ++i) vv[jb][i] = h2f(a.v16[vo + 64 * i]);
+      } else {
+        sum_splits<S, SMAX, SMAX>(a.v + vo, plane, SMAX, vv[jb]);
+#pragma unroll
+        for (int i = 0; i < S; ++i) c2[jb][i] = h2f(cs[64 * i]);
       }
+#pragma unroll
+      for (int i = 0; i < S; ++i) sg[jb][i] = h2f(ss[64 * i]);
     }
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
       if (p[jb] < 0) continue;
       const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), j0 + jb));
+      if constexpr (SMAX > 0) {
 #pragma unroll
-      for (int i = 0; i < S; ++i) vv[jb][i] *= c2[jb][i];
+        for (int i = 0; i < S; ++i) vv[jb][i] *= c2[jb][i];
+      }
       if (!a.rot.identity) fwht_segment<S>(vv[jb], lane);
 #pragma unroll
       for (int i = 0; i < S; ++i) acc[i] += wt * (vv[jb][i] * sg[jb][i]);
@@ -492,10 +518,9 @@ __global__ __launch_bounds__(64 * B) void k_combine_one_wide(CombineArgs a) {
   float v[4];
   if (p >= 0) {
     const size_t plane = static_cast<size_t>(a.routes) * n;
-    sum_splits<4, SMAX, splits_unroll<4, SMAX>(1)>(a.v + static_cast<size_t>(p) * n + off, plane, SMAX, v);
+    const size_t vo = static_cast<size_t>(p) * n + off;
     const uint16_t* c2 = a.scale2 + static_cast<size_t>(e) * n + off;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] *= h2f(c2[64 * i]);
+    scaled_values<4, SMAX, (SMAX > 0 ? splits_unroll<4, SMAX>(1) : 1)>(a.v + vo, a.v16 + vo, plane, SMAX, c2, v);
     if (!a.rot.identity) fwht_segment<4>(v, lane);
   } else {
 #pragma unroll
@@ -565,9 +590,11 @@ __global__ __launch_bounds__(256) void k_debug_mxfp8(const float* in, long long 
 
 inline unsigned blocks_for(long long rows) { return static_cast<unsigned>((rows + 3) / 4); }
 
+// most = 0: one fp16 plane with the channel scale applied
 template <class F>
 void dispatch_smax(int most, F&& f) {
   switch (most) {
+    case 0: f(std::integral_constant<int, 0>{}); break;
     case 1: f(std::integral_constant<int, 1>{}); break;
     case 2: f(std::integral_constant<int, 2>{}); break;
     case 4: f(std::integral_constant<int, 4>{}); break;
@@ -595,10 +622,14 @@ void launch_act(const ActArgs& a_in, bool mx, hipStream_t s) {
   const long long zero_blocks = a.y_zero ? (a.y_count + 1023) / 1024 : 0;
   const unsigned grid = static_cast<unsigned>(a.act_blocks + zero_blocks);
   dispatch_epl(a.rot, [&](auto epl) {
-    dispatch_smax(a.nsplit, [&](auto sm) {
+    dispatch_smax(a.z16 ? 0 : a.nsplit, [&](auto sm) {
       constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;
-      if (mx) hipLaunchKernelGGL((k_act<E, true, SM>), dim3(grid), dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((k_act<E, false, SM>), dim3(grid), dim3(256), 0, s, a);
+      if constexpr (SM == 0) {
+        hipLaunchKernelGGL((k_act<E, false, 0>), dim3(grid), dim3(256), 0, s, a);   // fp16 operands only
+      } else {
+        if (mx) hipLaunchKernelGGL((k_act<E, true, SM>), dim3(grid), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_act<E, false, SM>), dim3(grid), dim3(256), 0, s, a);
+      }
     });
   });
 }
@@ -608,7 +639,7 @@ static int wide_rows_b(const RowRot& r) { return r.pow2 && r.n >= 1024 && r.n <=
 
 void launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.top_k == 1 && wide_rows_b(a.rot) != 0) {
-    dispatch_smax(a.nsplit, [&](auto sm) {
+    dispatch_smax(a.v16 ? 0 : a.nsplit, [&](auto sm) {
       constexpr int SM = decltype(sm)::value;
       switch (wide_rows_b(a.rot)) {
         case 4: hipLaunchKernelGGL((k_combine_one_wide<4, SM>), dim3(a.tokens), dim3(256), 0, s, a); break;
@@ -620,7 +651,7 @@ void launch_combine(const CombineArgs& a, hipStream_t s) {
   }
   if (!a.rot.pow2 && !a.split_segments) {
     const unsigned grid = blocks_for(static_cast<long long>(a.tokens) * row_segments(a.rot));
-    dispatch_smax(a.nsplit, [&](auto sm) {
+    dispatch_smax(a.v16 ? 0 : a.nsplit, [&](auto sm) {
       hipLaunchKernelGGL((k_combine_blocks<decltype(sm)::value>), dim3(grid), dim3(256), 0, s, a);
     });
     return;
@@ -631,7 +662,7 @@ void launch_combine(const CombineArgs& a, hipStream_t s) {
   const size_t lds = static_cast<size_t>(W + 1) * L * 4 + 4 * W;
   const dim3 grid(a.tokens, split ? row_segments(a.rot) : 1);
   dispatch_epl(a.rot, [&](auto epl) {
-    dispatch_smax(a.nsplit, [&](auto sm) {
+    dispatch_smax(a.v16 ? 0 : a.nsplit, [&](auto sm) {
       constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;
       hipLaunchKernelGGL((k_combine<E, SM>), grid, dim3(64 * W), lds, s, a);
     });

@@ -370,9 +370,28 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
 
   // the lane's row offset passes through an empty asm so the store offsets are not hoisted out of
   // the unit loop into VGPRs
-  float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
   int lane_off = 4 * grp * a.N;
   asm volatile("" : "+v"(lane_off));
+  if (a.out16) {
+    // one K split: the finished sums times the expert's channel scale, rounded once to fp16
+    const uint16_t* cs = a.oscale + static_cast<size_t>(t.x & 0xffffff) * a.N + nt0 * 16 + col;
+    float sc[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) sc[j] = h2f(cs[16 * j]);
+    _Float16* o = reinterpret_cast<_Float16*>(a.out16) + static_cast<size_t>(row0) * a.N + nt0 * 16 + col;
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (16 * g + 4 * grp + i < rows) {
+#pragma unroll
+          for (int j = 0; j < SPW; ++j)
+            o[lane_off + (16 * g + i) * a.N + 16 * j] = static_cast<_Float16>(acc[g][j][i] * sc[j]);
+        }
+      }
+    return;
+  }
+  float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
 #pragma unroll
   for (int g = 0; g < 8; ++g)
 #pragma unroll

@@ -118,7 +118,7 @@ void build_layout(tmoe_plan_s* p) {
   L.tile_e = take(4ull * p->max_tiles);
   L.tile_r0 = take(4ull * p->max_tiles);
   L.tile_rows = take(4ull * p->max_tiles);
-  L.scalars = take(32);                               // num_tiles, status, num_gtiles, splits[2], arm status
+  L.scalars = take(32);                               // num_tiles, status, num_gtiles, splits[2], arm status, half[2]
   L.gtiles = take(16ull * p->max_gtiles);
   L.wgc = take(4ull * ((R + kRouteChunk - 1) / kRouteChunk) * (p->E + 1));   // per-workgroup route counts
   L.a1 = take(2ull * R * fp16_pitch(p->H));           // fp16 (padded rows), or E4M3 + E8M0 planes
@@ -183,6 +183,14 @@ GemmShape gemm_shape(const tmoe_plan_s* p, long long R, int mg, bool fp8, int fc
   return g;
 }
 
+// GEMMs on 128-row tiles with one K split finish their sums in one launch: they apply the channel
+// scale in the epilogue and leave one fp16 plane, half the bytes of fp32 for the next launch to read.
+// The opt-in atomic FC2 adds into y instead of leaving v.
+void half_planes(int mg, const GemmShape (&sh)[2], bool atomic_fc2, bool (&half)[2]) {
+  half[0] = mg >= 8 && sh[0].most == 1;
+  half[1] = mg >= 8 && sh[1].most == 1 && !atomic_fc2;
+}
+
 int big_cols(const tmoe_plan_s* p, bool fp8) {
   if (fp8 || p->max_bits > 4) return 0;      // 128-row tiles: widths 2-4 only
   for (int c : {256, 128})
@@ -190,9 +198,10 @@ int big_cols(const tmoe_plan_s* p, bool fp8) {
   return 0;
 }
 
-// With `rot` set, the same launch also writes the rotated input operand of every route.
+// With `rot` set, the same launch also writes the rotated input operand of every route. half[i]:
+// GEMM i + 1 leaves one fp16 plane (published with the split counts).
 void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_rows, const GemmShape (&sh)[2],
-                       void* scratch, const RotateArgs* rot, bool fp8, hipStream_t st) {
+                       const bool (&half)[2], void* scratch, const RotateArgs* rot, bool fp8, hipStream_t st) {
   RouteMapArgs a;
   std::memset(&a, 0, sizeof(a));
   a.ids = ids;
@@ -215,6 +224,9 @@ void enqueue_route_map(const tmoe_plan_s* p, const void* ids, int T, int gemm_ro
   a.splits = at<int32_t>(scratch, p->lay.scalars) + 3;
   a.nsplit[0] = sh[0].most;
   a.nsplit[1] = sh[1].most;
+  a.half = at<int32_t>(scratch, p->lay.scalars) + 6;
+  a.nhalf[0] = half[0] ? 1 : 0;
+  a.nhalf[1] = half[1] ? 1 : 0;
   a.slot_expert = at<int32_t>(scratch, p->lay.slot_e);
   a.wg_counts = at<int32_t>(scratch, p->lay.wgc);
   a.gtiles = at<int4>(scratch, p->lay.gtiles);
@@ -328,6 +340,10 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   const int mg = choose_mg(R, p->E, big_cols(p, fp8));
   const int gemm_rows = tile_rows(mg);
   const GemmShape sh[2] = {gemm_shape(p, R, mg, fp8, 1), gemm_shape(p, R, mg, fp8, 2)};
+  // the FP32-atomic FC2 reduction adds into y, which the activation launch zeroes beforehand
+  const bool atomic_fc2 = p->fc2_reduce == TMOE_FC2_ATOMIC && fc2_atomic_fits(p, fp8);
+  bool half[2];
+  half_planes(mg, sh, atomic_fc2, half);
 
   const int32_t* sorted = at<int32_t>(scratch, p->lay.sorted);
   const int32_t* slot_expert = at<int32_t>(scratch, p->lay.slot_e);
@@ -356,7 +372,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
 
   (void)hipGetLastError();   // clear a stale error so the check below reports this call only
   auto on = [&](int stage) { return first <= stage && stage <= last; };
-  if (on(0)) enqueue_route_map(p, ids, T, gemm_rows, sh, scratch, &ra, fp8, s);
+  if (on(0)) enqueue_route_map(p, ids, T, gemm_rows, sh, half, scratch, &ra, fp8, s);
 
   GemmArgs g1;
   g1.payload = wt->payload;
@@ -373,6 +389,8 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g1.nsplit = sh[0].most;
   g1.routes = static_cast<int>(R);
   g1.arow = sorted;
+  g1.out16 = half[0] ? reinterpret_cast<uint16_t*>(z) : nullptr;
+  g1.oscale = wt->scale1;
   const int waves1 = sh[0].waves;
   if (on(1)) {
     if (fp8) launch_gemm_f8(g1, 1, p->uniform_bits, mg, waves1, s);
@@ -381,6 +399,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
 
   ActArgs aa;
   aa.z = z;
+  aa.z16 = g1.out16;
   aa.nsplit = sh[0].most;
   aa.slot_expert = slot_expert;
   aa.scale1 = wt->scale1;
@@ -391,8 +410,6 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   aa.b_scale = bs;
   aa.ldb = fp16_pitch(p->I);
   aa.routes = static_cast<int>(R);
-  // the FP32-atomic FC2 reduction adds into y, which the activation launch zeroes beforehand
-  const bool atomic_fc2 = p->fc2_reduce == TMOE_FC2_ATOMIC && fc2_atomic_fits(p, fp8);
   aa.y_zero = atomic_fc2 ? y : nullptr;
   aa.y_count = atomic_fc2 ? static_cast<long long>(T) * p->H : 0;
   aa.act_blocks = 0;
@@ -408,6 +425,8 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g2.lda = fp16_pitch(p->I);
   g2.nsplit = sh[1].most;
   g2.arow = nullptr;
+  g2.out16 = half[1] ? reinterpret_cast<uint16_t*>(v) : nullptr;
+  g2.oscale = wt->scale2;
   const int waves2 = sh[1].waves;
   if (on(3) && atomic_fc2) {
     Fc2AtomicArgs fa;
@@ -434,6 +453,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
 
   CombineArgs ca;
   ca.v = v;
+  ca.v16 = g2.out16;
   ca.nsplit = sh[1].most;
   ca.ids = ids;
   ca.ids64 = p->ids64;
@@ -686,8 +706,10 @@ tmoe_status tmoe_build_route_map(tmoe_plan_t p, const void* ids, int32_t T, void
   const int mg = choose_mg(R, p->E, big_cols(p, false));
   const int gemm_rows = tile_rows(mg);
   const GemmShape sh[2] = {gemm_shape(p, R, mg, false, 1), gemm_shape(p, R, mg, false, 2)};
+  bool half[2];
+  half_planes(mg, sh, p->fc2_reduce == TMOE_FC2_ATOMIC && fc2_atomic_fits(p, false), half);
   (void)hipGetLastError();
-  enqueue_route_map(p, ids, T, gemm_rows, sh, scratch, nullptr, false, static_cast<hipStream_t>(stream));
+  enqueue_route_map(p, ids, T, gemm_rows, sh, half, scratch, nullptr, false, static_cast<hipStream_t>(stream));
   *view = make_view(p, scratch);
   return hipGetLastError() == hipSuccess ? TMOE_OK : TMOE_ERR_HIP;
 }
@@ -783,6 +805,7 @@ tmoe_status tmoe_debug_get_views(tmoe_plan_t p, int32_t T, int32_t w4a8, void* s
   out->v = at<float>(scratch, p->lay.v);
   out->splits = at<int32_t>(scratch, p->lay.scalars) + 3;
   out->arm_status = at<int32_t>(scratch, p->lay.scalars) + 5;
+  out->half_planes = at<int32_t>(scratch, p->lay.scalars) + 6;
   out->a1_pitch = w4a8 ? p->H : fp16_pitch(p->H);
   out->b_pitch = w4a8 ? p->I : fp16_pitch(p->I);
   return TMOE_OK;

@@ -28,6 +28,8 @@ struct RouteMapArgs {
   int32_t* num_gtiles;
   int32_t* splits;          // [2] K splits of FC1 and FC2, published for the consumers and tests
   int nsplit[2];            // the host's split counts
+  int32_t* half;            // [2] 1 where that GEMM leaves one fp16 plane with its channel scale applied
+  int nhalf[2];             //   (published like splits; null: not published)
   int32_t* slot_expert;     // [R]: expert of each slot, -1 past the filled slots
   int32_t* wg_counts;       // [workgroups][E + 1]: per-workgroup counts (large batches; E = invalid)
   ExpertInfo* einfo;
@@ -61,6 +63,7 @@ struct RotateArgs {          // a = R_H(su1_e * x_t) per route, fp16 or MXFP8, r
 
 struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_I(z_u)))
   const float* z;            // [nsplit][R][2I] unscaled partial sums
+  const uint16_t* z16 = nullptr;  // or (one K split): fp16 [R][2I], scale1 already applied
   int nsplit;                // FC1 K splits: 1, 2, 4 or 8
   const int32_t* slot_expert;  // [R]: expert of each slot, -1 past the filled slots
   const uint16_t* scale1;    // [E][2I]
@@ -78,6 +81,7 @@ struct ActArgs {             // b = R_I(su2 * silu(sv1g * R_I(z_g)) * (sv1u * R_
 
 struct CombineArgs {         // y_t = sum_j w[t,j] * sv2_e * R_H(scale2_e * v_slot), j ascending
   const float* v;            // [nsplit][R][H] FC2 partial sums (read only)
+  const uint16_t* v16 = nullptr;  // or (one K split): fp16 [R][H], scale2 already applied
   int nsplit;                // FC2 K splits: 1, 2, 4 or 8
   const void* ids;
   int ids64;
@@ -101,6 +105,8 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
   const int32_t* arow;       // operand row of each slot (FC1: the slot's route), or null: row = slot
   const uint8_t* a_scale;    // [R][K/32] (fp8 only)
   float* out;                // [splits][R][N]
+  uint16_t* out16 = nullptr; // 128-row tiles with one K split may instead leave fp16 [R][N] of
+  const uint16_t* oscale = nullptr;  //   out * oscale[e][n] (the channel scale, [E][N]), rounded once
   const int4* gtiles;
   const int32_t* num_gtiles;
   int nsplit;                // K splits of this GEMM (the host's choice, also published in splits[])

@@ -54,7 +54,8 @@ class PlanInfo(ctypes.Structure):
 
 class DebugViews(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("a1", "a1_scale", "z", "b", "b_scale", "v", "splits")] + \
-               [("a1_pitch", ctypes.c_int32), ("b_pitch", ctypes.c_int32), ("arm_status", ctypes.c_void_p)]
+               [("a1_pitch", ctypes.c_int32), ("b_pitch", ctypes.c_int32), ("arm_status", ctypes.c_void_p),
+                ("half_planes", ctypes.c_void_p)]
 
 
 class LinearConfig(ctypes.Structure):
