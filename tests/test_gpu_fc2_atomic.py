@@ -1,6 +1,9 @@
 """The opt-in FP32-atomic FC2 reduction (plan field fc2_reduce = atomic) against the float64 oracle.
 The order of the atomic additions is not fixed, so results are compared within the W4A16 bound,
-and with each other within fp32 rounding, never bit for bit."""
+and with each other within fp32 rounding, never bit for bit. Where the deterministic plan stores FC2's
+output as one fp16 plane (128-row tiles with one K split), the two paths also differ by that rounding,
+2^-11 relative per element of each route row before the output rotation (measured 2.1e-4 max-relative
+at prefill); those cases allow 2^-9, four times the rounding unit."""
 import dataclasses
 
 import numpy as np
@@ -9,6 +12,7 @@ import torch
 
 import oracle_np as O
 from gpu_cases import TOL_W4A16, Case, rel_err, say
+from trellis_quantized_moe_tmoe_amd.layer import scratch_view
 
 pytestmark = pytest.mark.gpu
 
@@ -22,9 +26,13 @@ class AtomicCase(Case):
         self.scratch = self.plan.alloc_scratch()
 
     def run_det(self):
-        y = self.det.forward(self.x, self.ids, self.w, self.weights, self.det.alloc_scratch())
+        """Deterministic plan's output and whether it left FC2's sums as one fp16 plane."""
+        scratch = self.det.alloc_scratch()
+        y = self.det.forward(self.x, self.ids, self.w, self.weights, scratch)
         torch.cuda.synchronize()
-        return y
+        v = self.det.debug_views(self.inp.tokens, False, scratch)
+        half = bool(scratch_view(scratch, v.half_planes, (2,), torch.int32)[1].item())
+        return y, half
 
 
 @pytest.mark.parametrize("name,T,over", [
@@ -39,10 +47,11 @@ def test_fc2_atomic_w4a16(name, T, over):
     c = AtomicCase(name, T, **over)
     y = c.run().cpu().numpy()
     err = rel_err(y, c.oracle_w4a16)
-    d = rel_err(y, c.run_det().cpu().numpy())
-    say(f"[result] {c.label} atomic FC2 rel err {err:.3e} (vs deterministic path {d:.3e})")
+    y_det, half = c.run_det()
+    d = rel_err(y, y_det.cpu().numpy())
+    say(f"[result] {c.label} atomic FC2 rel err {err:.3e} (vs deterministic path {d:.3e}, fp16 v plane {half})")
     assert err <= TOL_W4A16
-    assert d <= 1e-4
+    assert d <= (2.0 ** -9 if half else 1e-4)
 
 
 def test_fc2_atomic_identity_mode():
@@ -98,7 +107,7 @@ def test_fc2_atomic_graph_replays_zero_y_each_time():
 def test_fc2_atomic_falls_back_where_it_does_not_apply():
     # rows of 256 values (and W4A8) keep the deterministic epilogue: bit-identical to the default plan
     c = AtomicCase("tiny", 4)
-    assert torch.equal(c.run(), c.run_det())
+    assert torch.equal(c.run(), c.run_det()[0])
     c8 = AtomicCase("w4a8", 8)
     y8 = c8.run(w4a8=True)
     from trellis_quantized_moe_tmoe_amd import layer as L
