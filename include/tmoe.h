@@ -125,7 +125,15 @@ typedef struct {                 /* sizes derived from a plan */
 } tmoe_plan_info;
 
 /* Validate a configuration and build a plan (host only: no HIP call, no device allocation).
- * scratch_bytes / payload_words may be NULL. Errors: INVALID_ARG, UNSUPPORTED. */
+ * The plan fixes the geometry, the per-expert widths and the token capacity once and declares the
+ * size of the caller's scratch arena, so every later call is checked on the host and enqueues
+ * kernels only ("TrellisMX (procedural NPK) ... P8 runtime", flashinfer PR #69, description: the
+ * plan/arena split with a declared arena size, int32 or int64 ids, smallm_max_tokens; b12x PR
+ * #129 Summary: caller-owned storage, fail closed). The tile rule of 16*bits words per 16x16 tile
+ * and the widths follow the sparkinfer PR #90 reviews of prepare.py and kernel.py. Configuration
+ * errors: INVALID_ARG (null or out-of-range field), UNSUPPORTED (a shape or width this library
+ * does not implement). The plan is owned by the caller until tmoe_plan_destroy.
+ * scratch_bytes / payload_words may be NULL. */
 tmoe_status tmoe_plan(const tmoe_config *cfg, tmoe_plan_t *out, size_t *scratch_bytes,
                       size_t *payload_words);
 tmoe_status tmoe_plan_destroy(tmoe_plan_t plan);
@@ -141,9 +149,17 @@ tmoe_status tmoe_plan_expert_offset(tmoe_plan_t plan, int32_t expert, size_t *wo
 tmoe_status tmoe_build_route_map(tmoe_plan_t plan, const void *topk_ids, int32_t T, void *scratch,
                                  size_t scratch_bytes, tmoe_route_map *view_out, void *stream);
 
-/* The layer with fp16 activations and trellis weights decoded to fp16 MFMA operands.
+/* The layer with fp16 activations and trellis weights decoded to fp16 MFMA operands: the W4A16
+ * routed MoE of "integrate EXL3 Trellis into the fused W4A16 API" (sparkinfer PR #90: Summary and
+ * the kernel.py review for the epilogue order) with the launch structure of b12x PR #129 (Hot
+ * path: one rotation + quantization launch, the route map reused by FC1 and FC2, route-major FC1
+ * and FC2, exact top-k weighting into an FP32 output). Five launches on `stream`: route map with
+ * the input rotation, FC1, activation with the intermediate rotation, FC2, output rotation with
+ * the combine (one launch when the plan's smallm_max_tokens admits T).
  * x: bf16 [T][H] (16-byte aligned); topk_ids [T][k]; topk_w: fp32 [T][k]; y: fp32 [T][H]
- * (16-byte aligned), fully overwritten. Deterministic: repeated calls give identical bits. */
+ * (16-byte aligned), fully overwritten. Errors (nothing enqueued): INVALID_ARG (null pointer,
+ * T < 0), CAPACITY (T > max_tokens), SCRATCH (arena short or misaligned), ALIGNMENT, HIP (a launch
+ * failed). Deterministic with the default fc2_reduce: repeated calls give identical bits. */
 tmoe_status tmoe_forward_w4a16(tmoe_plan_t plan, const void *x_bf16, const void *topk_ids,
                                const float *topk_w, int32_t T, const tmoe_weights *weights,
                                float *y, void *scratch, size_t scratch_bytes, void *stream);
