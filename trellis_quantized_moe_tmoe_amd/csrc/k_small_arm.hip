@@ -614,12 +614,11 @@ __device__ __forceinline__ bool arm_unit_f16(const ArmArgs& a, const ArmLds& L, 
   const bool stager2 = NL == 2 && c2 < BW / 4;
   const int st2_off = ((c2 / (ANS * CPT)) * NT + (c2 / CPT) % ANS) * TW + 4 * (c2 % CPT);
   const int kstride = 2 * NT * TW;
-  const int j0 = BITS >= 5 ? half_window_word<BITS>(2 * q) : window_word<BITS>(q);
-  const int rd_a = (grp >> 1) * ANS * TW + (j0 < 0 ? j0 + TW : j0);
-  const int rd_b = (grp >> 1) * ANS * TW + ((j0 + 1 == TW) ? 0 : j0 + 1);
-  const int j1 = BITS >= 5 ? half_window_word<BITS>(2 * q + 1) : 0;
-  const int rd_c = (grp >> 1) * ANS * TW + (j1 < 0 ? j1 + TW : j1);
-  const int rd_d = (grp >> 1) * ANS * TW + ((j1 + 1 == TW) ? 0 : j1 + 1);
+  constexpr int NWW = dec_words<BITS>();
+  const uint32_t dsh = dec_shift<BITS>(q);
+  int rd[NWW];
+#pragma unroll
+  for (int i = 0; i < NWW; ++i) rd[i] = (grp >> 1) * ANS * TW + (dec_first_word<BITS>(q) + i + TW) % TW;
   const int slot_row = g.row0 + min(col, g.rows - 1);
   const long long arow = FC == 1 ? L.sorted[slot_row] : slot_row;
   const long long aoff = arow * lda + 8 * grp;
@@ -652,27 +651,15 @@ __device__ __forceinline__ bool arm_unit_f16(const ArmArgs& a, const ArmLds& L, 
     else
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((ADF - 1) * (NL + 1)) : "memory");
     const uint32_t* slot = ring + d * STAGE;
-    uint32_t wh[ANS], wl[ANS], wc[ANS], wd[ANS];
+    uint32_t w[ANS][NWW];
 #pragma unroll
-    for (int ns = 0; ns < ANS; ++ns) {
-      wh[ns] = slot[rd_a + ns * TW];
-      wl[ns] = slot[rd_b + ns * TW];
-      if constexpr (BITS >= 5) {
-        wc[ns] = slot[rd_c + ns * TW];
-        wd[ns] = slot[rd_d + ns * TW];
-      }
-    }
+    for (int ns = 0; ns < ANS; ++ns)
+#pragma unroll
+      for (int i = 0; i < NWW; ++i) w[ns][i] = slot[rd[i] + ns * TW];
     const half8 av = *reinterpret_cast<const half8*>(slot + AOFF + 4 * lane);
     half8 b[ANS];
 #pragma unroll
-    for (int ns = 0; ns < ANS; ++ns) {
-      if constexpr (BITS >= 5) {
-        const uint32_t w4[4] = {wh[ns], wl[ns], wc[ns], wd[ns]};
-        b[ns] = decode8_wide<BITS>(w4, q, mask, orv);
-      } else {
-        b[ns] = decode8<BITS>(wh[ns], wl[ns], q, mask, orv);
-      }
-    }
+    for (int ns = 0; ns < ANS; ++ns) b[ns] = decode8<BITS>(w[ns], dsh, mask, orv);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     issue_w(next, d);
     issue_a(next, d);
@@ -704,12 +691,13 @@ __device__ __forceinline__ bool arm_unit_f16(const ArmArgs& a, const ArmLds& L, 
 
 // 32 E4M3 weights of one lane for one 128-deep K step (as the scaled-fp8 GEMM launch).
 template <int BITS>
-__device__ __forceinline__ i8v arm_decode_b_f8(const uint32_t (&w)[8], int col, uint32_t mask, uint32_t orv) {
+__device__ __forceinline__ i8v arm_decode_b_f8(const uint32_t (&w)[4][dec_words<BITS>()], const uint32_t (&sh)[2],
+                                               uint32_t mask, uint32_t orv) {
   i8v b;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     uint32_t p[4];
-    decode8_pairs<BITS>(w[2 * g], w[2 * g + 1], 2 * col + (g & 1), mask, orv, p);
+    decode8_pairs<BITS>(w[g], sh[g & 1], mask, orv, p);
     b[2 * g] = static_cast<int>(fp8x4_from_pairs(p[0], p[1]));
     b[2 * g + 1] = static_cast<int>(fp8x4_from_pairs(p[2], p[3]));
   }
@@ -744,19 +732,21 @@ __device__ __forceinline__ bool arm_unit_f8(const ArmArgs& a, const ArmLds& L, c
   f4 acc[ANS];
 #pragma unroll
   for (int ns = 0; ns < ANS; ++ns) acc[ns] = f4{0.f, 0.f, 0.f, 0.f};
-  uint32_t w[D8][ANS][8];
+  constexpr int NWW = dec_words<BITS>();
+  const uint32_t dsh[2] = {dec_shift<BITS>(2 * col), dec_shift<BITS>(2 * col + 1)};
+  uint32_t w[D8][ANS][4][NWW];
   unsigned long long alo[D8][2], ahi[D8][2];
   int asc[D8];
-  auto load_w = [&](int ks, uint32_t(&ww)[ANS][8]) {
+  auto load_w = [&](int ks, uint32_t(&ww)[ANS][4][NWW]) {
     const int kt0 = 8 * ks + grp;
     const uint32_t* r0 = mat + static_cast<size_t>(kt0 * NT + nt0) * TW;
     const uint32_t* r1 = mat + static_cast<size_t>((kt0 + 4) * NT + nt0) * TW;
 #pragma unroll
     for (int ns = 0; ns < ANS; ++ns) {
-      load_window<BITS>(r0 + ns * TW, 2 * col, ww[ns][0], ww[ns][1]);
-      load_window<BITS>(r0 + ns * TW, 2 * col + 1, ww[ns][2], ww[ns][3]);
-      load_window<BITS>(r1 + ns * TW, 2 * col, ww[ns][4], ww[ns][5]);
-      load_window<BITS>(r1 + ns * TW, 2 * col + 1, ww[ns][6], ww[ns][7]);
+      load_dec_words<BITS>(r0 + ns * TW, 2 * col, ww[ns][0]);
+      load_dec_words<BITS>(r0 + ns * TW, 2 * col + 1, ww[ns][1]);
+      load_dec_words<BITS>(r1 + ns * TW, 2 * col, ww[ns][2]);
+      load_dec_words<BITS>(r1 + ns * TW, 2 * col + 1, ww[ns][3]);
     }
   };
   auto load_a = [&](int ks, unsigned long long (&lo)[2], unsigned long long (&hi)[2], int& sc) {
@@ -777,7 +767,7 @@ __device__ __forceinline__ bool arm_unit_f8(const ArmArgs& a, const ArmLds& L, c
       if (base + d < ks1) {
         i8v b[ANS];
 #pragma unroll
-        for (int ns = 0; ns < ANS; ++ns) b[ns] = arm_decode_b_f8<BITS>(w[d][ns], col, mask, orv);
+        for (int ns = 0; ns < ANS; ++ns) b[ns] = arm_decode_b_f8<BITS>(w[d][ns], dsh, mask, orv);
         i8v av = i8v{static_cast<int>(alo[d][0]), static_cast<int>(alo[d][0] >> 32), static_cast<int>(alo[d][1]),
                      static_cast<int>(alo[d][1] >> 32), static_cast<int>(ahi[d][0]), static_cast<int>(ahi[d][0] >> 32),
                      static_cast<int>(ahi[d][1]), static_cast<int>(ahi[d][1] >> 32)};

@@ -97,14 +97,12 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
   const bool stager2 = NL == 2 && c2 < BW / 4;
   const int st2_off = ((c2 / (NS * CPT)) * NT + (c2 / CPT) % NS) * TW + 4 * (c2 % CPT);
   const int kstride = 2 * NT * TW;                                            // words between K steps
-  // reading: window words of group q in tile row (grp>>1) of strip ns (widths 5, 6: the two half
-  // windows of the group, tmoe_device.hpp)
-  const int j0 = BITS >= 5 ? half_window_word<BITS>(2 * q) : window_word<BITS>(q);
-  const int rd_a = (grp >> 1) * NS * TW + (j0 < 0 ? j0 + TW : j0);
-  const int rd_b = (grp >> 1) * NS * TW + ((j0 + 1 == TW) ? 0 : j0 + 1);
-  const int j1 = BITS >= 5 ? half_window_word<BITS>(2 * q + 1) : 0;
-  const int rd_c = (grp >> 1) * NS * TW + (j1 < 0 ? j1 + TW : j1);
-  const int rd_d = (grp >> 1) * NS * TW + ((j1 + 1 == TW) ? 0 : j1 + 1);
+  // reading: the words of group q in tile row (grp>>1) of strip ns (tmoe_device.hpp, state windows)
+  constexpr int NWW = dec_words<BITS>();
+  const uint32_t dsh = dec_shift<BITS>(q);
+  int rd[NWW];
+#pragma unroll
+  for (int i = 0; i < NWW; ++i) rd[i] = (grp >> 1) * NS * TW + (dec_first_word<BITS>(q) + i + TW) % TW;
   long long aoff[MG];
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg) aoff[mg] = operand_row(a, row0 + min(16 * mg + col, rows - 1)) * a.lda + 8 * grp;
@@ -141,29 +139,17 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
     // the direct loads of the DF-1 younger steps may still be in flight
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DF - 1) * (NL + MG)) : "memory");
     const uint32_t* slot = ring + d * STAGE;
-    uint32_t wh[NS], wl[NS], wc[NS], wd[NS];           // wc, wd: second half windows (widths 5, 6)
+    uint32_t w[NS][NWW];
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      wh[ns] = slot[rd_a + ns * TW];
-      wl[ns] = slot[rd_b + ns * TW];
-      if constexpr (BITS >= 5) {
-        wc[ns] = slot[rd_c + ns * TW];
-        wd[ns] = slot[rd_d + ns * TW];
-      }
-    }
+    for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+      for (int i = 0; i < NWW; ++i) w[ns][i] = slot[rd[i] + ns * TW];
     half8 aa[MG];
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) aa[mg] = *reinterpret_cast<const half8*>(slot + AOFF + mg * 256 + 4 * lane);
     half8 b[NS];
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      if constexpr (BITS >= 5) {
-        const uint32_t w4[4] = {wh[ns], wl[ns], wc[ns], wd[ns]};
-        b[ns] = decode8_wide<BITS>(w4, q, mask, orv);
-      } else {
-        b[ns] = decode8<BITS>(wh[ns], wl[ns], q, mask, orv);
-      }
-    }
+    for (int ns = 0; ns < NS; ++ns) b[ns] = decode8<BITS>(w[ns], dsh, mask, orv);
     // every LDS read of this slot has returned before the slot is refilled
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     issue(next, d);
@@ -259,11 +245,13 @@ constexpr int BIG_D = 4;                       // ring depth in K steps (3 in fl
 constexpr int BIG_A_U4 = 8 * 64;               // 16-byte chunks of A per step (8 KB)
 
 template <int SPW>
-constexpr int big_w_u4() { return 4 * SPW * 16; }     // trellis-word chunks per step, sized for 4 bits
+constexpr int big_w_u4() { return 4 * 64; }     // trellis-word chunks per step: 1 KB per wavefront
 template <int SPW>
 constexpr int big_slot_u4() { return BIG_A_U4 + big_w_u4<SPW>(); }
 
-template <int BITS, int SPW>
+// NGR: 16-row groups computed, 8 for a full 128-row tile or 4 for a tile of at most 64 rows, whose
+// upper four groups would only repeat its last row: those take neither MFMAs nor A loads.
+template <int BITS, int SPW, int NGR>
 __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, int nb, int s, int splits, int lane,
                                              int wv, uint4* ring, uint32_t mask, uint32_t orv) {
   constexpr int TW = 8 * BITS;                   // 32-bit words per tile
@@ -280,34 +268,41 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
   const gptr<uint32_t> mat = uniform_ptr(reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS) +
                                          static_cast<size_t>(nt0) * TW);
   const gptr<_Float16> A = uniform_ptr(static_cast<const _Float16*>(a.a));
-  // A rows copied by this wavefront: row groups 2 * wv and 2 * wv + 1, in MFMA operand order
-  long long aoff[2];
+  // A rows copied by this wavefront: row groups GPW * wv .. GPW * wv + GPW - 1, in MFMA operand order
+  static_assert(NGR == 8 || NGR == 4, "row groups: 8 or 4");
+  constexpr int GPW = NGR / 4;                   // row groups copied per wavefront
+  constexpr int LPS = GPW + 1;                   // loads per step and wavefront (A groups + words)
+  long long aoff[GPW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) aoff[i] = operand_row(a, row0 + min(16 * (2 * wv + i) + col, rows - 1)) * a.lda + 8 * grp;
-  // trellis words: per step two tile rows x SPW adjacent tiles = two runs of RUN words; lane
-  // L < RUN / 2 copies 16-byte piece L % (RUN / 4) of run L / (RUN / 4)
-  const bool stager = lane < RUN / 2;
-  const int st_run = lane / (RUN / 4), st_piece = lane % (RUN / 4);
+  for (int i = 0; i < GPW; ++i) aoff[i] = operand_row(a, row0 + min(16 * (GPW * wv + i) + col, rows - 1)) * a.lda + 8 * grp;
+  // trellis words: per step two tile rows x SPW adjacent tiles = two runs of RUN words in RUN / 2
+  // 16-byte pieces; lane L copies piece L mod (RUN / 2), piece p % (RUN / 4) of run p / (RUN / 4),
+  // to byte 16 L of the wavefront's 1 KB staging area. Every lane loads, so the staging load has no
+  // branch around it (a branch lets the compiler merge loads of different paths, whose LDS
+  // addresses then no longer match); lanes L >= RUN / 2 write copies past the words read back.
+  const int st_p = lane % (RUN / 2);
+  const int st_run = st_p / (RUN / 4), st_piece = st_p % (RUN / 4);
   const int st_src = st_run * NT * TW + 4 * st_piece;            // words, relative to the step
-  // window words of group q in tile row (grp >> 1) of strip j: [run][strip][TW] in the slot
-  const int j0 = window_word<BITS>(q);
-  const int rd_a = (grp >> 1) * RUN + (j0 < 0 ? j0 + TW : j0);
-  const int rd_b = (grp >> 1) * RUN + ((j0 + 1 == TW) ? 0 : j0 + 1);
+  // words of group q in tile row (grp >> 1) of strip j: [run][strip][TW] in the slot
+  constexpr int NWW = dec_words<BITS>();
+  const uint32_t dsh = dec_shift<BITS>(q);
+  int rd[NWW];
+#pragma unroll
+  for (int i = 0; i < NWW; ++i) rd[i] = (grp >> 1) * RUN + (dec_first_word<BITS>(q) + i + TW) % TW;
 
   auto issue = [&](int ks, int slot) {
     uint4* sl = ring + slot * SLOT;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < GPW; ++i)
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(A + 32 * ks + aoff[i]),
-                                       (void __attribute__((address_space(3)))*)(sl + (2 * wv + i) * 64), 16, 0, 0);
-    if (stager)
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(mat + static_cast<size_t>(2 * ks) * NT * TW + st_src),
-                                       (void __attribute__((address_space(3)))*)(sl + BIG_A_U4 + wv * SPW * 16), 16, 0, 0);
+                                       (void __attribute__((address_space(3)))*)(sl + (GPW * wv + i) * 64), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(mat + static_cast<size_t>(2 * ks) * NT * TW + st_src),
+                                     (void __attribute__((address_space(3)))*)(sl + BIG_A_U4 + wv * 64), 16, 0, 0);
   };
 
-  f4 acc[8][SPW];
+  f4 acc[NGR][SPW];
 #pragma unroll
-  for (int g = 0; g < 8; ++g)
+  for (int g = 0; g < NGR; ++g)
 #pragma unroll
     for (int j = 0; j < SPW; ++j) acc[g][j] = f4{0.f, 0.f, 0.f, 0.f};
 
@@ -316,20 +311,25 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
   // The weights of step ks are decoded during step ks - 1, interleaved with its MFMAs (scheduling
   // groups below), so the VALU work of one step overlaps the matrix work of the step before.
   auto decode_slot = [&](int slot, half8 (&bb)[SPW]) {
-    const uint32_t* ws = reinterpret_cast<const uint32_t*>(ring + slot * SLOT + BIG_A_U4 + wv * SPW * 16);
+    const uint32_t* ws = reinterpret_cast<const uint32_t*>(ring + slot * SLOT + BIG_A_U4 + wv * 64);
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) bb[j] = decode8<BITS>(ws[rd_a + j * TW], ws[rd_b + j * TW], q, mask, orv);
+    for (int j = 0; j < SPW; ++j) {
+      uint32_t w[NWW];
+#pragma unroll
+      for (int i = 0; i < NWW; ++i) w[i] = ws[rd[i] + j * TW];
+      bb[j] = decode8<BITS>(w, dsh, mask, orv);
+    }
   };
   half8 b0[SPW], b1[SPW];
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * (BIG_D - 2)) : "memory");   // step ks0 is in
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS * (BIG_D - 2)) : "memory");   // step ks0 is in
   decode_slot(0, b0);
   int slot = 0;
   // One K step: MFMAs on b (decoded during the step before) while decoding the next step into nb.
   auto step = [&](int ks, half8 (&b)[SPW], half8 (&nb)[SPW]) {
-    // Step ks + 1 has landed (only step ks + 2's three loads may be in flight) and this wavefront's
+    // Step ks + 1 has landed (only step ks + 2's LPS loads may be in flight) and this wavefront's
     // LDS reads are done; a plain barrier (no fence: a fence would also wait for the younger loads)
     // then publishes steps ks and ks + 1 and frees the slot of step ks - 1.
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(3 * (BIG_D - 3)) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LPS * (BIG_D - 3)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");                          // no LDS access moves above the barrier
     const int refill = slot == 0 ? BIG_D - 1 : slot - 1;
@@ -337,24 +337,24 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
     const uint4* sl = ring + slot * SLOT;
     slot = slot + 1 == BIG_D ? 0 : slot + 1;
     // next step's words (the slot of step ks + 1; after the last step a stale slot, decoded unused)
-    const uint32_t* wsn = reinterpret_cast<const uint32_t*>(ring + slot * SLOT + BIG_A_U4 + wv * SPW * 16);
-    uint32_t wh[SPW], wl[SPW];
+    const uint32_t* wsn = reinterpret_cast<const uint32_t*>(ring + slot * SLOT + BIG_A_U4 + wv * 64);
+    uint32_t wn[SPW][NWW];
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      wh[j] = wsn[rd_a + j * TW];
-      wl[j] = wsn[rd_b + j * TW];
-    }
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+      for (int i = 0; i < NWW; ++i) wn[j][i] = wsn[rd[i] + j * TW];
     half8 av = *reinterpret_cast<const half8*>(sl + lane);
     __builtin_amdgcn_sched_barrier(0);
-    // Eight pieces, kept in this order: the next A fragment's LDS read, this row group's SPW MFMAs
-    // and, spread over the pieces, one strip of the next step's decode at a time.
+    // NGR pieces, kept in this order: the next A fragment's LDS read, this row group's SPW MFMAs
+    // and, spread over the pieces, the next step's decode one strip (or, with four pieces and four
+    // strips, one strip per piece) at a time.
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const half8 an = g + 1 < 8 ? *reinterpret_cast<const half8*>(sl + (g + 1) * 64 + lane) : av;
+    for (int g = 0; g < NGR; ++g) {
+      const half8 an = g + 1 < NGR ? *reinterpret_cast<const half8*>(sl + (g + 1) * 64 + lane) : av;
 #pragma unroll
       for (int j = 0; j < SPW; ++j) acc[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[j], acc[g][j], 0, 0, 0);
-      constexpr int every = 8 / SPW;
-      if (g % every == every - 1) nb[g / every] = decode8<BITS>(wh[g / every], wl[g / every], q, mask, orv);
+      constexpr int every = NGR / SPW > 0 ? NGR / SPW : 1;
+      if (g % every == every - 1) nb[g / every] = decode8<BITS>(wn[g / every], dsh, mask, orv);
       av = an;
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -380,7 +380,7 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
     for (int j = 0; j < SPW; ++j) sc[j] = h2f(cs[16 * j]);
     _Float16* o = reinterpret_cast<_Float16*>(a.out16) + static_cast<size_t>(row0) * a.N + nt0 * 16 + col;
 #pragma unroll
-    for (int g = 0; g < 8; ++g)
+    for (int g = 0; g < NGR; ++g)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (16 * g + 4 * grp + i < rows) {
@@ -393,7 +393,7 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
   }
   float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
 #pragma unroll
-  for (int g = 0; g < 8; ++g)
+  for (int g = 0; g < NGR; ++g)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (16 * g + 4 * grp + i < rows) {
@@ -401,6 +401,34 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
         for (int j = 0; j < SPW; ++j) o[lane_off + (16 * g + i) * a.N + 16 * j] = acc[g][j][i];   // < 2^31
       }
     }
+}
+
+// A unit body as a separate function: the mixed-width kernel holds six bodies (three widths, two
+// row-group counts), and inlining them all lets values hoisted above the width switch stay live
+// through every body and spill inside the K loops.
+// The launch arguments reach it through memory: they are copied into registers first and those
+// loads are complete before the unit's first staging load, so the unit's constant wait counts still
+// count its own staging loads only.
+template <int BITS, int SPW, int NGR>
+__device__ __attribute__((noinline)) void unit_f16_big_call(const GemmArgs& a, const int4 t, int nb, int s, int splits,
+                                                            int lane, int wv, uint4* ring, uint32_t mask, uint32_t orv) {
+  const GemmArgs la = a;
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  unit_f16_big<BITS, SPW, NGR>(la, t, nb, s, splits, lane, wv, ring, mask, orv);
+}
+
+// One unit at the tile's width (BITS = 0: experts of mixed widths 2-4, read from the tile).
+template <int BITS, int SPW, int NGR>
+__device__ __forceinline__ void big_unit_width(const GemmArgs& a, const int4 t, int nb, int s, int splits, int lane,
+                                               int wv, uint4* ring, uint32_t mask, uint32_t orv) {
+  if constexpr (BITS != 0) {
+    unit_f16_big<BITS, SPW, NGR>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+  } else {
+    const int bits = __builtin_amdgcn_readfirstlane((t.x >> 24) & 0xff);
+    if (bits == 4) unit_f16_big_call<4, SPW, NGR>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    else if (bits == 3) unit_f16_big_call<3, SPW, NGR>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    else unit_f16_big_call<2, SPW, NGR>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+  }
 }
 
 // Units (tile, 64*SPW-column block, K split) are dealt to workgroups. Workgroups are dealt to the
@@ -428,26 +456,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPW >= 4 ? 
     const int rest = u / splits;
     const int nb = rest % NB;
     const int4 t = a.gtiles[rest / NB];
-    if constexpr (BITS != 0) {
-      unit_f16_big<BITS, SPW>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
-    } else {
-      const int bits = (t.x >> 24) & 0xff;
-      if (bits == 4) unit_f16_big<4, SPW>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
-      else if (bits == 3) unit_f16_big<3, SPW>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
-      else unit_f16_big<2, SPW>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
-    }
+    if (__builtin_amdgcn_readfirstlane(t.z) > 64) big_unit_width<BITS, SPW, 8>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    else big_unit_width<BITS, SPW, 4>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
   }
 }
 
 // 32 E4M3 weights of one lane for one 128-deep K step: tiles kt0 (bytes 0-15) and kt0+4
 // (bytes 16-31) of one column, 16 consecutive elements of each (groups 2*col and 2*col+1).
+// w[g] holds the words of group 2*col + (g & 1) of tile kt0 (g < 2) or kt0+4 (g >= 2); sh[g & 1] is
+// that group's window shift.
 template <int BITS>
-__device__ __forceinline__ i8v decode_b_f8(const uint32_t (&w)[8], int col, uint32_t mask, uint32_t orv) {
+__device__ __forceinline__ i8v decode_b_f8(const uint32_t (&w)[4][dec_words<BITS>()], const uint32_t (&sh)[2],
+                                           uint32_t mask, uint32_t orv) {
   i8v b;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     uint32_t p[4];
-    decode8_pairs<BITS>(w[2 * g], w[2 * g + 1], 2 * col + (g & 1), mask, orv, p);
+    decode8_pairs<BITS>(w[g], sh[g & 1], mask, orv, p);
     b[2 * g] = static_cast<int>(fp8x4_from_pairs(p[0], p[1]));
     b[2 * g + 1] = static_cast<int>(fp8x4_from_pairs(p[2], p[3]));
   }
@@ -486,19 +511,21 @@ __device__ __forceinline__ void unit_f8(const GemmArgs& a, const int4 t, int ng,
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) acc[mg][ns] = f4{0.f, 0.f, 0.f, 0.f};
 
-  uint32_t w[D8][NS][8];
+  constexpr int NWW = dec_words<BITS>();
+  const uint32_t dsh[2] = {dec_shift<BITS>(2 * col), dec_shift<BITS>(2 * col + 1)};
+  uint32_t w[D8][NS][4][NWW];
   uint4 alo[D8][MG], ahi[D8][MG];
   int asc[D8][MG];
-  auto load = [&](int ks, uint32_t(&ww)[NS][8], uint4(&lo)[MG], uint4(&hi)[MG], int(&sc)[MG]) {
+  auto load = [&](int ks, uint32_t(&ww)[NS][4][NWW], uint4(&lo)[MG], uint4(&hi)[MG], int(&sc)[MG]) {
     const int kt0 = 8 * ks + grp;
     const uint32_t* r0 = mat + static_cast<size_t>(kt0 * NT + nt0) * TW;
     const uint32_t* r1 = mat + static_cast<size_t>((kt0 + 4) * NT + nt0) * TW;
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
-      load_window<BITS>(r0 + ns * TW, 2 * col, ww[ns][0], ww[ns][1]);
-      load_window<BITS>(r0 + ns * TW, 2 * col + 1, ww[ns][2], ww[ns][3]);
-      load_window<BITS>(r1 + ns * TW, 2 * col, ww[ns][4], ww[ns][5]);
-      load_window<BITS>(r1 + ns * TW, 2 * col + 1, ww[ns][6], ww[ns][7]);
+      load_dec_words<BITS>(r0 + ns * TW, 2 * col, ww[ns][0]);
+      load_dec_words<BITS>(r0 + ns * TW, 2 * col + 1, ww[ns][1]);
+      load_dec_words<BITS>(r1 + ns * TW, 2 * col, ww[ns][2]);
+      load_dec_words<BITS>(r1 + ns * TW, 2 * col + 1, ww[ns][3]);
     }
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) {
@@ -515,7 +542,7 @@ __device__ __forceinline__ void unit_f8(const GemmArgs& a, const int4 t, int ng,
       if (base + d < ks1) {
         i8v b[NS];
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) b[ns] = decode_b_f8<BITS>(w[d][ns], col, mask, orv);
+        for (int ns = 0; ns < NS; ++ns) b[ns] = decode_b_f8<BITS>(w[d][ns], dsh, mask, orv);
         i8v av[MG];
         int sa[MG];
 #pragma unroll
@@ -622,9 +649,11 @@ __device__ __forceinline__ void fc2_atomic_unit(const Fc2AtomicArgs& fa, const i
   const bool stager2 = NL == 2 && c2 < BW / 4;
   const int st2_off = ((c2 / (FNS * CPT)) * NT + (c2 / CPT) % FNS) * TW + 4 * (c2 % CPT);
   const int kstride = 2 * NT * TW;
-  const int j0 = window_word<BITS>(q);
-  const int rd_a = (grp >> 1) * FNS * TW + (j0 < 0 ? j0 + TW : j0);
-  const int rd_b = (grp >> 1) * FNS * TW + ((j0 + 1 == TW) ? 0 : j0 + 1);
+  constexpr int NWW = dec_words<BITS>();
+  const uint32_t dsh = dec_shift<BITS>(q);
+  int rd[NWW];
+#pragma unroll
+  for (int i = 0; i < NWW; ++i) rd[i] = (grp >> 1) * FNS * TW + (dec_first_word<BITS>(q) + i + TW) % TW;
   long long aoff[MG];
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg) aoff[mg] = static_cast<long long>(row0 + min(16 * mg + col, rows - 1)) * a.lda + 8 * grp;
@@ -656,18 +685,17 @@ __device__ __forceinline__ void fc2_atomic_unit(const Fc2AtomicArgs& fa, const i
   auto step = [&](int d, int next) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DF - 1) * (NL + MG)) : "memory");
     const uint32_t* slot = ring + d * STAGE;
-    uint32_t wh[FNS], wl[FNS];
+    uint32_t w[FNS][NWW];
 #pragma unroll
-    for (int ns = 0; ns < FNS; ++ns) {
-      wh[ns] = slot[rd_a + ns * TW];
-      wl[ns] = slot[rd_b + ns * TW];
-    }
+    for (int ns = 0; ns < FNS; ++ns)
+#pragma unroll
+      for (int i = 0; i < NWW; ++i) w[ns][i] = slot[rd[i] + ns * TW];
     half8 aa[MG];
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) aa[mg] = *reinterpret_cast<const half8*>(slot + AOFF + mg * 256 + 4 * lane);
     half8 b[FNS];
 #pragma unroll
-    for (int ns = 0; ns < FNS; ++ns) b[ns] = decode8<BITS>(wh[ns], wl[ns], q, mask, orv);
+    for (int ns = 0; ns < FNS; ++ns) b[ns] = decode8<BITS>(w[ns], dsh, mask, orv);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     issue(next, d);
 #pragma unroll
@@ -766,16 +794,9 @@ __global__ __launch_bounds__(256) void k_debug_decode(const uint16_t* words, int
   const uint32_t* tile = reinterpret_cast<const uint32_t*>(words) + static_cast<size_t>(kt * NT + nt) * TW;
   const uint32_t mask = vreg_const(kMcgMask);
   uint32_t p[4];
-  if constexpr (BITS >= 5) {
-    uint32_t w[4];
-    load_window_half<BITS>(tile, 2 * q, w[0], w[1]);
-    load_window_half<BITS>(tile, 2 * q + 1, w[2], w[3]);
-    decode8_pairs_wide<BITS>(w[0], w[1], w[2], w[3], q, mask, kMcgOr, p);
-  } else {
-    uint32_t hi, lo;
-    load_window<BITS>(tile, q, hi, lo);
-    decode8_pairs<BITS>(hi, lo, q, mask, kMcgOr, p);
-  }
+  uint32_t w[dec_words<BITS>()];
+  load_dec_words<BITS>(tile, q, w);
+  decode8_pairs<BITS>(w, dec_shift<BITS>(q), mask, kMcgOr, p);
   const int k0 = 16 * kt + 8 * (grp & 1);
   const int n = 16 * nt + col;
   if (!as_e4m3) {

@@ -1,6 +1,6 @@
 // tmoe_device.hpp -- device building blocks shared by the HIP kernels (gfx950 / CDNA4).
 //
-//  * trellis window decode: 8 consecutive tile elements per lane, from two aligned 32-bit
+//  * trellis window decode: 8 consecutive tile elements per lane, from two or three aligned 32-bit
 //    loads, straight into a register operand (trellis3_t256 tiles, "integrate EXL3 Trellis into
 //    the fused W4A16 API", review of prepare.py; codebook constants from the review of
 //    intrinsics.py);
@@ -64,83 +64,95 @@ __device__ __forceinline__ _Float16 trellis_code(uint32_t s) {
 // Two little-endian 16-bit words in one 32-bit load, as a big-endian (first word high) bit string.
 __device__ __forceinline__ uint32_t be32(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 16); }
 
-// 32-bit word index j0 (floor((q*BITS - 2) / 4), may be -1) of the 64-bit window that covers the
-// states of elements 8q .. 8q+7 of a tile: their bits span [8q*BITS + BITS - 16, 8q*BITS + 8*BITS).
+// ---- state windows
+// The states of elements 8q .. 8q+7 of a tile (group q) are the 16-bit stream fields starting at
+// bits s0 + jj*BITS, jj = 0..7, with s0 = 8q*BITS + BITS - 16 (taken modulo the tile's 256*BITS
+// bits). A lane reads the 32-bit words j0 .. j0 + dec_words - 1 (modulo the tile) that hold them.
+//  * 4 bits: j0 = q - 1 (the fields then end at fixed offsets of two words; see prep_window4);
+//  * other widths: j0 = floor((s0 - 1) / 32). The lane shifts the words once into a window that
+//    starts at s0 itself (a funnel shift by dec_shift, the same for every step of the lane), so
+//    every field sits at a fixed offset jj*BITS of the window and takes one bit-field extract. The
+//    window spans 64 bits (three words; two for width 2, whose fields span 30 bits), and the 8
+//    fields span 7*BITS + 16 <= 58 bits of it.
 template <int BITS>
-__device__ __forceinline__ int window_word(int q) {
+constexpr int dec_words() { return BITS == 4 || BITS == 2 ? 2 : 3; }
+
+template <int BITS>
+__device__ __forceinline__ int dec_first_word(int q) {
   if constexpr (BITS == 4) return q - 1;
-  else if constexpr (BITS == 2) return (q - 1) >> 1;
-  else return (q * BITS - 2) >> 2;
+  else return (8 * q * BITS + BITS - 17) >> 5;       // arithmetic shift: floor, -1 for q = 0
 }
 
-// Load the window of group q of the tile starting at `tile` (8*BITS 32-bit words): the raw words
-// holding stream bits [32*j0, 32*j0 + 64), taken modulo the tile length.
+// Right-shift amount of the funnel shift that starts the window at s0 (0..31; unused at 4 bits).
 template <int BITS>
-__device__ __forceinline__ void load_window(const uint32_t* __restrict__ tile, int q, uint32_t& hi,
-                                            uint32_t& lo) {
+__device__ __forceinline__ uint32_t dec_shift(int q) {
+  const int s0 = 8 * q * BITS + BITS - 16;
+  return static_cast<uint32_t>(32 - (s0 - 32 * dec_first_word<BITS>(q)));
+}
+
+// Read group q's words from a tile of 8*BITS 32-bit words (raw, as stored).
+template <int BITS>
+__device__ __forceinline__ void load_dec_words(const uint32_t* __restrict__ tile, int q,
+                                               uint32_t (&w)[dec_words<BITS>()]) {
   constexpr int NW = 8 * BITS;
-  const int j0 = window_word<BITS>(q);
-  const int a = j0 < 0 ? j0 + NW : j0;
-  const int b = (j0 + 1 == NW) ? 0 : j0 + 1;
-  hi = tile[a];
-  lo = tile[b];
+  const int j0 = dec_first_word<BITS>(q);
+#pragma unroll
+  for (int i = 0; i < dec_words<BITS>(); ++i) w[i] = tile[(j0 + i + NW) % NW];
 }
 
-// A loaded window (raw words) prepared so that each of its eight 16-bit states (elements 8q ..
-// 8q+7) takes one or two instructions: for 4 bits the big-endian strings X = w[2q-1]:w[2q] and
-// L = w[2q]:w[2q+1] plus the raw low word, for other widths both words as big-endian strings.
-template <int BITS>
-struct Window {
+// 4 bits: the big-endian strings X = w[2q-1]:w[2q] and L = w[2q]:w[2q+1] plus the raw low word.
+struct Window4 {
   uint32_t x, l, raw_lo;
 };
 
-template <int BITS>
-__device__ __forceinline__ Window<BITS> prep_window(uint32_t hi_raw, uint32_t lo_raw) {
-  Window<BITS> w;
-  if constexpr (BITS == 4) {
-    // words: hi_raw = w[2q-2] | w[2q-1] << 16, lo_raw = w[2q] | w[2q+1] << 16 (little endian)
-    w.x = __builtin_amdgcn_perm(hi_raw, lo_raw, 0x07060100u);   // bytes: lo.0 lo.1 hi.2 hi.3
-    w.l = be32(lo_raw);
-  } else {
-    w.x = be32(hi_raw);
-    w.l = be32(lo_raw);
-  }
+__device__ __forceinline__ Window4 prep_window4(uint32_t hi_raw, uint32_t lo_raw) {
+  // words: hi_raw = w[2q-2] | w[2q-1] << 16, lo_raw = w[2q] | w[2q+1] << 16 (little endian)
+  Window4 w;
+  w.x = __builtin_amdgcn_perm(hi_raw, lo_raw, 0x07060100u);   // bytes: lo.0 lo.1 hi.2 hi.3
+  w.l = be32(lo_raw);
   w.raw_lo = lo_raw;
   return w;
 }
 
-// State of element 8q+jj (jj a compile-time constant after unrolling).
+// The 16-bit states of group q from its words (raw, as stored); sh = dec_shift<BITS>(q).
 template <int BITS>
-__device__ __forceinline__ uint32_t window_state(const Window<BITS>& w, int q, int jj) {
+__device__ __forceinline__ void group_states(const uint32_t (&w)[dec_words<BITS>()], uint32_t sh, uint32_t (&st)[8]) {
   if constexpr (BITS == 4) {
     // the state of element 8q+j is the 16 stream bits ending at 4(8q+j+1): X >> (12-4j) for j < 3,
     // L >> (28-4j) for 4 <= j < 7, and the raw half-words for j = 3 and 7
-    if (jj == 3) return w.raw_lo & 0xffffu;
-    if (jj == 7) return w.raw_lo >> 16;
-    return jj < 3 ? __builtin_amdgcn_ubfe(w.x, 12 - 4 * jj, 16) : __builtin_amdgcn_ubfe(w.l, 28 - 4 * jj, 16);
+    const Window4 v = prep_window4(w[0], w[1]);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (jj == 3) st[jj] = v.raw_lo & 0xffffu;
+      else if (jj == 7) st[jj] = v.raw_lo >> 16;
+      else st[jj] = jj < 3 ? __builtin_amdgcn_ubfe(v.x, 12 - 4 * jj, 16) : __builtin_amdgcn_ubfe(v.l, 28 - 4 * jj, 16);
+    }
   } else {
-    const int j0 = window_word<BITS>(q);
-    // element 8q+jj's state ends at stream bit (8q+jj+1)*BITS, i.e. end_rel bits into the window
-    const int shift = 64 - ((8 * q + jj + 1) * BITS - 32 * j0);
-    const uint32_t v = shift >= 32 ? (w.x >> (shift - 32)) : __builtin_amdgcn_alignbit(w.x, w.l, shift);
-    return v & 0xffffu;
+    // window bits [0, 32) in X, [32, 64) in L, [16, 48) in M (bit 0 = the window's first stream bit,
+    // held in bit 31 of X); field jj starts at window bit o = jj*BITS
+    const uint32_t w0 = be32(w[0]), w1 = be32(w[1]);
+    const uint32_t X = __builtin_amdgcn_alignbit(w0, w1, sh);
+    uint32_t L = 0, M = 0;
+    if constexpr (dec_words<BITS>() == 3) {
+      L = __builtin_amdgcn_alignbit(w1, be32(w[2]), sh);
+      M = __builtin_amdgcn_alignbit(X, L, 16);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int o = jj * BITS;
+      if (o <= 16) st[jj] = __builtin_amdgcn_ubfe(X, 16 - o, 16);
+      else if (o <= 32) st[jj] = __builtin_amdgcn_ubfe(M, 32 - o, 16);
+      else st[jj] = __builtin_amdgcn_ubfe(L, 48 - o, 16);
+    }
   }
 }
 
-// The 16-bit states of elements 8q .. 8q+7 from a loaded window (raw words).
+// Decode group q into four packed fp16 pairs (element 8q+2i in the low half of p[i]).
 template <int BITS>
-__device__ __forceinline__ void window_states(uint32_t hi_raw, uint32_t lo_raw, int q, uint32_t (&st)[8]) {
-  const Window<BITS> w = prep_window<BITS>(hi_raw, lo_raw);
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) st[jj] = window_state<BITS>(w, q, jj);
-}
-
-// Decode elements 8q .. 8q+7 into four packed fp16 pairs (element 8q+2i in the low half of p[i]).
-template <int BITS>
-__device__ __forceinline__ void decode8_pairs(uint32_t hi_raw, uint32_t lo_raw, int q, uint32_t mask,
+__device__ __forceinline__ void decode8_pairs(const uint32_t (&w)[dec_words<BITS>()], uint32_t sh, uint32_t mask,
                                               uint32_t orv, uint32_t (&p)[4]) {
   uint32_t st[8];
-  window_states<BITS>(hi_raw, lo_raw, q, st);
+  group_states<BITS>(w, sh, st);
   uint32_t m[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) m[j] = mcg_bits(st[j], mask, orv);
@@ -149,62 +161,10 @@ __device__ __forceinline__ void decode8_pairs(uint32_t hi_raw, uint32_t lo_raw, 
 }
 
 template <int BITS>
-__device__ __forceinline__ half8 decode8(uint32_t hi_raw, uint32_t lo_raw, int q, uint32_t mask, uint32_t orv) {
+__device__ __forceinline__ half8 decode8(const uint32_t (&w)[dec_words<BITS>()], uint32_t sh, uint32_t mask,
+                                         uint32_t orv) {
   uint32_t p[4];
-  decode8_pairs<BITS>(hi_raw, lo_raw, q, mask, orv, p);
-  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-  const u4v v = {p[0], p[1], p[2], p[3]};
-  return __builtin_bit_cast(half8, v);
-}
-
-// Widths 5 and 6. The states of eight consecutive elements span up to 7*BITS + 16 = 58 stream bits,
-// which one window of two 32-bit words does not hold at every offset, so a group of eight is read
-// as two halves of four (elements 8q..8q+3 = half 2q, 8q+4..8q+7 = half 2q+1). A half's states span
-// 3*BITS + 16 bits starting at most 30 bits into the word holding its first bit (the start offsets
-// 20h - 11 and 24h - 10 modulo 32 never exceed 29 and 30), so the two words from there hold it.
-template <int BITS>
-__device__ __forceinline__ int half_window_word(int h) {
-  return ((4 * h + 1) * BITS - 16) >> 5;            // floor: negative for h = 0 (the stream wraps)
-}
-
-// Raw words (j0, j0 + 1) of half h's window in a tile of 8*BITS words, indices modulo the tile.
-template <int BITS>
-__device__ __forceinline__ void load_window_half(const uint32_t* __restrict__ tile, int h, uint32_t& hi,
-                                                 uint32_t& lo) {
-  constexpr int NW = 8 * BITS;
-  const int j0 = half_window_word<BITS>(h);
-  hi = tile[j0 < 0 ? j0 + NW : j0];
-  lo = tile[j0 + 1 == NW ? 0 : j0 + 1];
-}
-
-// State of element 4h+jj from its half's window, both words as big-endian strings (x first).
-template <int BITS>
-__device__ __forceinline__ uint32_t half_state(uint32_t x, uint32_t l, int h, int jj) {
-  const int shift = 64 - ((4 * h + jj + 1) * BITS - 32 * half_window_word<BITS>(h));   // 0..48
-  const uint32_t v = shift >= 32 ? (x >> (shift - 32)) : __builtin_amdgcn_alignbit(x, l, shift);
-  return v & 0xffffu;
-}
-
-// Elements 8q .. 8q+7 (widths 5, 6) from the raw windows of halves 2q (h0) and 2q+1 (h1), as four
-// packed fp16 pairs (element 8q+2i in the low half of p[i]).
-template <int BITS>
-__device__ __forceinline__ void decode8_pairs_wide(uint32_t h0_hi, uint32_t h0_lo, uint32_t h1_hi, uint32_t h1_lo,
-                                                   int q, uint32_t mask, uint32_t orv, uint32_t (&p)[4]) {
-  const uint32_t x0 = be32(h0_hi), l0 = be32(h0_lo), x1 = be32(h1_hi), l1 = be32(h1_lo);
-  uint32_t m[8];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    m[jj] = mcg_bits(half_state<BITS>(x0, l0, 2 * q, jj), mask, orv);
-    m[4 + jj] = mcg_bits(half_state<BITS>(x1, l1, 2 * q + 1, jj), mask, orv);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = code_pair(m[2 * i], m[2 * i + 1]);
-}
-
-template <int BITS>
-__device__ __forceinline__ half8 decode8_wide(const uint32_t (&w)[4], int q, uint32_t mask, uint32_t orv) {
-  uint32_t p[4];
-  decode8_pairs_wide<BITS>(w[0], w[1], w[2], w[3], q, mask, orv, p);
+  decode8_pairs<BITS>(w, sh, mask, orv, p);
   typedef uint32_t u4v __attribute__((ext_vector_type(4)));
   const u4v v = {p[0], p[1], p[2], p[3]};
   return __builtin_bit_cast(half8, v);
