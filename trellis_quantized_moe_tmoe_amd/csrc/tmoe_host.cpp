@@ -165,8 +165,11 @@ struct GemmShape {          // launch shape of one grouped GEMM
 // Column groups, K steps, split bound and launch size of FC1 (fc = 1) or FC2 (fc = 2). For 16- to
 // 64-row tiles a unit is one wavefront's 64 columns and `waves` counts persistent wavefronts; for
 // 128-row tiles a unit is one workgroup's 128 or 256 columns and `waves` counts workgroups.
-GemmShape gemm_shape(const tmoe_plan_s* p, long long R, int mg, bool fp8, int fc) {
+int fc2_mg(const tmoe_plan_s* p, int mg);
+
+GemmShape gemm_shape(const tmoe_plan_s* p, long long R, int mg_in, bool fp8, int fc) {
   GemmShape g;
+  const int mg = fc == 2 ? fc2_mg(p, mg_in) : mg_in;
   const int K = fc == 1 ? p->H : p->I;
   const int N = fc == 1 ? 2 * p->I : p->H;
   const bool big = mg >= 8;
@@ -191,12 +194,17 @@ void half_planes(int mg, const GemmShape (&sh)[2], bool atomic_fc2, bool (&half)
   half[1] = mg >= 8 && sh[1].most == 1 && !atomic_fc2;
 }
 
+// FC1's workgroup tile width for 128-row tiles (both GEMMs' widths must be multiples of 128, as
+// they share the tile list), or 0.
 int big_cols(const tmoe_plan_s* p, bool fp8) {
   if (fp8 || p->max_bits > 4) return 0;      // 128-row tiles: widths 2-4 only
-  for (int c : {256, 128})
-    if (p->H % c == 0 && (2 * p->I) % c == 0) return c;
-  return 0;
+  if (p->H % 128 != 0 || (2 * p->I) % 128 != 0) return 0;
+  return (2 * p->I) % 256 == 0 ? 256 : 128;
 }
+
+// FC2's tile shape code: its own workgroup tile width (H = 2560 with 2I = 640 takes 256 columns
+// for FC2 and 128 for FC1).
+int fc2_mg(const tmoe_plan_s* p, int mg) { return mg >= 8 ? (p->H % 256 == 0 ? 16 : 8) : mg; }
 
 // With `rot` set, the same launch also writes the rotated input operand of every route. half[i]:
 // GEMM i + 1 leaves one fp16 plane (published with the split counts).
@@ -448,7 +456,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
     launch_fc2_atomic(fa, p->uniform_bits, mg2, static_cast<int>(std::min<long long>(units, 2048)), s);
   } else if (on(3)) {
     if (fp8) launch_gemm_f8(g2, 2, p->uniform_bits, mg, waves2, s);
-    else launch_gemm_f16(g2, 2, p->uniform_bits, mg, waves2, s);
+    else launch_gemm_f16(g2, 2, p->uniform_bits, fc2_mg(p, mg), waves2, s);
   }
 
   CombineArgs ca;
