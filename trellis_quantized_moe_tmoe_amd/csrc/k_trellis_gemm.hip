@@ -479,29 +479,32 @@ __device__ __forceinline__ i8v decode_b_f8(const uint32_t (&w)[4][dec_words<BITS
   return b;
 }
 
+// Ring words of one wavefront of the scaled-fp8 GEMM: D8 steps of 8 tile rows x NS strips, sized for
+// 4 bits (4 KB per step).
+constexpr int kF8StepWords = 8 * NS * 8 * 4;
+
 template <int BITS, int MG>
 __device__ __forceinline__ void unit_f8(const GemmArgs& a, const int4 t, int ng, int s, int splits, int lane,
-                                        uint32_t mask, uint32_t orv) {
+                                        uint32_t* ring, uint32_t mask, uint32_t orv) {
   constexpr int TW = 8 * BITS;
   const long long woff = (static_cast<long long>(static_cast<unsigned>(t.w)) << 8);
-  const uint32_t* mat = reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS);
   const int row0 = t.y, rows = t.z;
   const int NT = a.N >> 4;
   const int col = lane & 15, grp = lane >> 4;
   const int ksteps = (a.K >> 7) / splits;
   const int ks0 = s * ksteps, ks1 = ks0 + ksteps;
   const int nt0 = ng * NS;
+  const gptr<uint32_t> mat = uniform_ptr(reinterpret_cast<const uint32_t*>(a.payload + woff + a.fc2_words_per_bit * BITS) +
+                                         static_cast<size_t>(nt0) * TW);
   const uint8_t* A = static_cast<const uint8_t*>(a.a);
   const int kblocks = a.K >> 5;
 
   const uint8_t* arow[MG];
   const uint8_t* srow[MG];
-  bool aok[MG];
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg) {
     const int r = 16 * mg + col;
-    aok[mg] = r < rows;
-    const size_t rr = static_cast<size_t>(operand_row(a, row0 + (aok[mg] ? r : 0)));
+    const size_t rr = static_cast<size_t>(operand_row(a, row0 + (r < rows ? r : 0)));
     arow[mg] = A + rr * a.K + 16 * grp;
     srow[mg] = a.a_scale + rr * kblocks + grp;
   }
@@ -511,61 +514,89 @@ __device__ __forceinline__ void unit_f8(const GemmArgs& a, const int4 t, int ng,
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) acc[mg][ns] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // A step's trellis words (8 tile rows of NS adjacent tiles, NS*TW words each) arrive with BITS
+  // direct global->LDS loads per lane, 16 bytes each: piece c = 64 i + lane is 16-byte chunk c % (NS*TW/4)
+  // of tile row c / (NS*TW/4), written to ring word 4c ([tile row][strip][TW] order). A lane then reads
+  // the words of its four groups -- 2*col and 2*col+1 of tile rows grp and grp + 4 -- from the slot.
+  constexpr int CPR = NS * TW / 4;                     // 16-byte chunks per tile row
+  int st_src[BITS];
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) {
+    const int c = 64 * i + lane;
+    st_src[i] = (c / CPR) * NT * TW + 4 * (c % CPR);
+  }
   constexpr int NWW = dec_words<BITS>();
   const uint32_t dsh[2] = {dec_shift<BITS>(2 * col), dec_shift<BITS>(2 * col + 1)};
-  uint32_t w[D8][NS][4][NWW];
-  uint4 alo[D8][MG], ahi[D8][MG];
-  int asc[D8][MG];
-  auto load = [&](int ks, uint32_t(&ww)[NS][4][NWW], uint4(&lo)[MG], uint4(&hi)[MG], int(&sc)[MG]) {
-    const int kt0 = 8 * ks + grp;
-    const uint32_t* r0 = mat + static_cast<size_t>(kt0 * NT + nt0) * TW;
-    const uint32_t* r1 = mat + static_cast<size_t>((kt0 + 4) * NT + nt0) * TW;
+  int rd[4][NWW];
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      load_dec_words<BITS>(r0 + ns * TW, 2 * col, ww[ns][0]);
-      load_dec_words<BITS>(r0 + ns * TW, 2 * col + 1, ww[ns][1]);
-      load_dec_words<BITS>(r1 + ns * TW, 2 * col, ww[ns][2]);
-      load_dec_words<BITS>(r1 + ns * TW, 2 * col + 1, ww[ns][3]);
-    }
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < NWW; ++i)
+      rd[g][i] = (grp + 4 * (g >> 1)) * NS * TW + (dec_first_word<BITS>(2 * col + (g & 1)) + i + TW) % TW;
+  // A operands in the MFMA's register shape: bytes 0-15 from k = 16*grp + [0, 16) of the step, bytes
+  // 16-31 from k = 64 + 16*grp + [0, 16). Rows beyond the tile load row 0 of the tile instead; their
+  // output rows are never stored (an MFMA output row depends on its own A row and scale only).
+  i8v areg[D8][MG];
+  int asc[D8][MG];
+  auto issue = [&](int ks, int d) {
+    uint32_t* slot = ring + d * kF8StepWords;
+    const gptr<uint32_t> src = mat + static_cast<size_t>(8 * ks) * NT * TW;
+#pragma unroll
+    for (int i = 0; i < BITS; ++i)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src + st_src[i]),
+                                       (void __attribute__((address_space(3)))*)(slot + 256 * i), 16, 0, 0);
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) {
-      lo[mg] = *reinterpret_cast<const uint4*>(arow[mg] + 128 * ks);
-      hi[mg] = *reinterpret_cast<const uint4*>(arow[mg] + 128 * ks + 64);
-      sc[mg] = srow[mg][4 * ks];
+      typedef int i4v __attribute__((ext_vector_type(4)));
+      const i4v lo = *reinterpret_cast<const i4v*>(arow[mg] + 128 * ks);
+      const i4v hi = *reinterpret_cast<const i4v*>(arow[mg] + 128 * ks + 64);
+      areg[d][mg] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      asc[d][mg] = srow[mg][4 * ks];
     }
   };
+  auto step = [&](int d, int next) {
+    // the loads of the D8-1 younger steps may still be in flight
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((D8 - 1) * (BITS + 3 * MG)) : "memory");
+    const uint32_t* slot = ring + d * kF8StepWords;
+    i8v b[NS];
 #pragma unroll
-  for (int d = 0; d < D8; ++d) load(min(ks0 + d, ks1 - 1), w[d], alo[d], ahi[d], asc[d]);
-  for (int base = ks0; base < ks1; base += D8) {
+    for (int ns = 0; ns < NS; ++ns) {
+      uint32_t w[4][NWW];
 #pragma unroll
-    for (int d = 0; d < D8; ++d) {
-      if (base + d < ks1) {
-        i8v b[NS];
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) b[ns] = decode_b_f8<BITS>(w[d][ns], dsh, mask, orv);
-        i8v av[MG];
-        int sa[MG];
-#pragma unroll
-        for (int mg = 0; mg < MG; ++mg) {
-          const uint4 lo = alo[d][mg], hi = ahi[d][mg];
-          av[mg] = i8v{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                       static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
-          sa[mg] = asc[d][mg];
-          if (!aok[mg]) {
-            av[mg] = i8v{0, 0, 0, 0, 0, 0, 0, 0};
-            sa[mg] = 127;
-          }
-        }
-        load(min(base + d + D8, ks1 - 1), w[d], alo[d], ahi[d], asc[d]);
-#pragma unroll
-        for (int mg = 0; mg < MG; ++mg)
-#pragma unroll
-          for (int ns = 0; ns < NS; ++ns)
-            acc[mg][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[mg], b[ns], acc[mg][ns], 0, 0, 0,
-                                                                          sa[mg], 0, 127);
-      }
+        for (int i = 0; i < NWW; ++i) w[g][i] = slot[rd[g][i] + ns * TW];
+      b[ns] = decode_b_f8<BITS>(w, dsh, mask, orv);
     }
+    i8v av[MG];
+    int sa[MG];
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) {
+      av[mg] = areg[d][mg];
+      sa[mg] = asc[d][mg];
+    }
+    // every LDS read of this slot has returned before the slot is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue(next, d);
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+        acc[mg][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[mg], b[ns], acc[mg][ns], 0, 0, 0,
+                                                                      sa[mg], 0, 127);
+  };
+#pragma unroll
+  for (int d = 0; d < D8; ++d) issue(min(ks0 + d, ks1 - 1), d);
+  int base = ks0;
+  for (; base + D8 <= ks1; base += D8) {
+#pragma unroll
+    for (int d = 0; d < D8; ++d) step(d, min(base + d + D8, ks1 - 1));
   }
+#pragma unroll
+  for (int d = 0; d < D8; ++d)
+    if (base + d < ks1) step(d, ks1 - 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // no load may still target the ring
+
   float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg)
@@ -581,7 +612,10 @@ __device__ __forceinline__ void unit_f8(const GemmArgs& a, const int4 t, int ng,
 
 template <int BITS, int MG, int FC>
 __global__ __launch_bounds__(256) void k_gemm_f8(GemmArgs a) {
+  __shared__ uint32_t ring_all[4 * D8 * kF8StepWords];
   const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t* ring = ring_all + wv * D8 * kF8StepWords;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int W = gridDim.x * 4;
   const int NG = a.N / (16 * NS);
@@ -594,12 +628,12 @@ __global__ __launch_bounds__(256) void k_gemm_f8(GemmArgs a) {
     const int ng = rest % NG;
     const int4 t = a.gtiles[rest / NG];
     if constexpr (BITS != 0) {
-      unit_f8<BITS, MG>(a, t, ng, s, splits, lane, mask, orv);
+      unit_f8<BITS, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
     } else {
       const int bits = (t.x >> 24) & 0xff;
-      if (bits == 4) unit_f8<4, MG>(a, t, ng, s, splits, lane, mask, orv);
-      else if (bits == 3) unit_f8<3, MG>(a, t, ng, s, splits, lane, mask, orv);
-      else unit_f8<2, MG>(a, t, ng, s, splits, lane, mask, orv);
+      if (bits == 4) unit_f8<4, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
+      else if (bits == 3) unit_f8<3, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
+      else unit_f8<2, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
     }
   }
 }

@@ -193,9 +193,10 @@ __device__ __forceinline__ uint32_t fp8x2_from_f32(float a, float b) {
 }
 
 // Two packed fp16 pairs -> four E4M3 bytes in one word (pa's values in bytes 0-1, pb's in 2-3);
-// the second conversion writes the high half and keeps the low one.
+// the second conversion writes the high half and keeps the low one. The first starts from pa's own
+// bits (its high half is overwritten), so no register has to be cleared for it.
 __device__ __forceinline__ uint32_t fp8x4_from_pairs(uint32_t pa, uint32_t pb) {
-  s2v r = {0, 0};
+  s2v r = __builtin_bit_cast(s2v, pa);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(half2v, pa), 1.0f, false);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(half2v, pb), 1.0f, true);
   return __builtin_bit_cast(uint32_t, r);
