@@ -68,13 +68,13 @@ def parse():
 class Bench:
     """One workload: inputs, weight copies, plan and scratch on the device."""
 
-    def __init__(self, name: str, T: int, w4a8: bool, **plan_kw):
+    def __init__(self, name: str, T: int, w4a8: bool, bits_override=None, **plan_kw):
         import torch
         from trellis_quantized_moe_tmoe_amd import layer as L
         from trellis_quantized_moe_tmoe_amd.workloads import make_inputs
         self.torch, self.L = torch, L
         self.name, self.T, self.w4a8 = name, T, w4a8
-        self.inp = make_inputs(name, tokens=T)
+        self.inp = make_inputs(name, tokens=T, bits_override=bits_override)
         self.plan = L.Plan.for_inputs(self.inp, **plan_kw)
         base = L.DeviceWeights.from_inputs(self.inp)
         per_copy = sum(getattr(base, f).numel() * getattr(base, f).element_size() for f in base.FIELDS)
@@ -487,6 +487,17 @@ def main():
                             "algorithmic_flops": e.flops_fc2, "avg_launch_ms": k2["fc2"]}}
             if w8:
                 w8_out[t] = (e.inp, e.output())
+            del e
+            torch.cuda.empty_cache()
+        # the prefill geometry with 5- and 6-bit trellis weights (same routes and activations)
+        for bo in (5, 6):
+            e = Bench("prefill", 2048, False, bits_override=bo)
+            rr = e.run(max(5, args.steps // 5), 3)
+            k2 = rr["kernel_ms"]
+            tf = (e.flops_fc1 + e.flops_fc2) / ((k2["fc1"] + k2["fc2"]) * 1e-3) / 1e12
+            extra[f"prefill:2048 bits {bo}"] = {"tokens_per_s": 2048 / (rr["ms_step"] * 1e-3), "ms_per_step": rr["ms_step"],
+                                                "gemm_tflops": tf, "gemm_tflops_frac": tf / MFMA_F16_PEAK_TFLOPS,
+                                                "stage_ms": rr["stage_ms"], "kernel_ms": k2}
             del e
             torch.cuda.empty_cache()
         # the single-launch small-batch arm (plan field smallm_max_tokens) against the five launches

@@ -205,6 +205,10 @@ def test_layer_w4a16_workgroup_tiles_with_k_splits(T):
     ("tiny", 450, dict(experts=4, top_k=2)),   # ~225 rows per expert
     ("tiny", 600, dict()),                     # 8 experts of ~150 rows
     ("wide", 300, dict(hidden=256, inter=128, experts=4, top_k=2)),   # mixed 2/3/4-bit experts
+    ("tiny", 450, dict(experts=4, top_k=2, bits_override=5)),         # 5-bit experts: two staging loads
+    ("tiny", 600, dict(bits_override=6)),                             # 6-bit experts
+    ("tiny", 450, dict(hidden=512, inter=256, experts=6, top_k=2, bits_choices=(2, 3, 4, 5, 6))),  # mixed 2-6
+    ("tiny", 300, dict(hidden=384, inter=192, experts=4, top_k=2, bits_override=6)),  # 128-column tiles, 6 bits
 ])
 def test_layer_w4a16_workgroup_tile_edges(name, T, over):
     c = Case(name, T, **over)

@@ -244,18 +244,27 @@ __global__ __launch_bounds__(256) void k_gemm_f16(GemmArgs a) {
 constexpr int BIG_D = 4;                       // ring depth in K steps (3 in flight)
 constexpr int BIG_A_U4 = 8 * 64;               // 16-byte chunks of A per step (8 KB)
 
-template <int SPW>
-constexpr int big_w_u4() { return 4 * 64; }     // trellis-word chunks per step: 1 KB per wavefront
-template <int SPW>
-constexpr int big_slot_u4() { return BIG_A_U4 + big_w_u4<SPW>(); }
+// Words of one step of a wavefront: two tile rows of SPW tiles of up to RB bits, staged in NLB
+// loads of 64 16-byte pieces (1 KB each): one load up to 4 bits, two at 5 and 6 bits with 4 strips.
+template <int SPW, int RB>
+constexpr int big_loads() { return (2 * SPW * 8 * RB / 4 + 63) / 64; }
+template <int SPW, int RB>
+constexpr int big_w_u4() { return 4 * 64 * big_loads<SPW, RB>(); }   // 16-byte chunks per step
+template <int SPW, int RB>
+constexpr int big_slot_u4() { return BIG_A_U4 + big_w_u4<SPW, RB>(); }
+// Ring width of a kernel instantiated at width code BITS (mixed 2-4 and 2-6 sized for 4 and 6).
+template <int BITS>
+constexpr int big_ring_bits() { return BITS == kMixedWide ? 6 : (BITS > 4 ? BITS : 4); }
 
 // NGR: 16-row groups computed, 8 for a full 128-row tile or 4 for a tile of at most 64 rows, whose
 // upper four groups would only repeat its last row: those take neither MFMAs nor A loads.
-template <int BITS, int SPW, int NGR>
+template <int BITS, int SPW, int NGR, int RB>
 __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, int nb, int s, int splits, int lane,
                                              int wv, uint4* ring, uint32_t mask, uint32_t orv) {
   constexpr int TW = 8 * BITS;                   // 32-bit words per tile
-  constexpr int SLOT = big_slot_u4<SPW>();
+  constexpr int SLOT = big_slot_u4<SPW, RB>();
+  constexpr int NLB = big_loads<SPW, RB>();      // staging loads per step and wavefront
+  constexpr int WREG = 64 * NLB;                 // 16-byte chunks of a wavefront's staging area
   constexpr int RUN = SPW * TW;                  // words of one tile row of this wavefront's strips
   const long long woff = (static_cast<long long>(static_cast<unsigned>(t.w)) << 8);
   const int row0 = t.y, rows = t.z;
@@ -271,18 +280,23 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
   // A rows copied by this wavefront: row groups GPW * wv .. GPW * wv + GPW - 1, in MFMA operand order
   static_assert(NGR == 8 || NGR == 4, "row groups: 8 or 4");
   constexpr int GPW = NGR / 4;                   // row groups copied per wavefront
-  constexpr int LPS = GPW + 1;                   // loads per step and wavefront (A groups + words)
+  constexpr int LPS = GPW + NLB;                 // loads per step and wavefront (A groups + words)
+  static_assert(2 * SPW * TW / 4 <= WREG, "a step's words fit the staging area");
   long long aoff[GPW];
 #pragma unroll
   for (int i = 0; i < GPW; ++i) aoff[i] = operand_row(a, row0 + min(16 * (GPW * wv + i) + col, rows - 1)) * a.lda + 8 * grp;
   // trellis words: per step two tile rows x SPW adjacent tiles = two runs of RUN words in RUN / 2
-  // 16-byte pieces; lane L copies piece L mod (RUN / 2), piece p % (RUN / 4) of run p / (RUN / 4),
-  // to byte 16 L of the wavefront's 1 KB staging area. Every lane loads, so the staging load has no
-  // branch around it (a branch lets the compiler merge loads of different paths, whose LDS
-  // addresses then no longer match); lanes L >= RUN / 2 write copies past the words read back.
-  const int st_p = lane % (RUN / 2);
-  const int st_run = st_p / (RUN / 4), st_piece = st_p % (RUN / 4);
-  const int st_src = st_run * NT * TW + 4 * st_piece;            // words, relative to the step
+  // 16-byte pieces; load i of lane L copies piece (64 i + L) mod (RUN / 2) -- piece p % (RUN / 4)
+  // of run p / (RUN / 4) -- to byte 16 (64 i + L) of the wavefront's staging area. Every lane loads,
+  // so the staging loads have no branch around them (a branch lets the compiler merge loads of
+  // different paths, whose LDS addresses then no longer match); pieces past RUN / 2 are copies
+  // written beyond the words read back.
+  int st_src[NLB];
+#pragma unroll
+  for (int i = 0; i < NLB; ++i) {
+    const int st_p = (64 * i + lane) % (RUN / 2);
+    st_src[i] = (st_p / (RUN / 4)) * NT * TW + 4 * (st_p % (RUN / 4));   // words, relative to the step
+  }
   // words of group q in tile row (grp >> 1) of strip j: [run][strip][TW] in the slot
   constexpr int NWW = dec_words<BITS>();
   const uint32_t dsh = dec_shift<BITS>(q);
@@ -296,8 +310,10 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
     for (int i = 0; i < GPW; ++i)
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(A + 32 * ks + aoff[i]),
                                        (void __attribute__((address_space(3)))*)(sl + (GPW * wv + i) * 64), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(mat + static_cast<size_t>(2 * ks) * NT * TW + st_src),
-                                     (void __attribute__((address_space(3)))*)(sl + BIG_A_U4 + wv * 64), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NLB; ++i)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(mat + static_cast<size_t>(2 * ks) * NT * TW + st_src[i]),
+                                       (void __attribute__((address_space(3)))*)(sl + BIG_A_U4 + wv * WREG + 64 * i), 16, 0, 0);
   };
 
   f4 acc[NGR][SPW];
@@ -311,7 +327,7 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
   // The weights of step ks are decoded during step ks - 1, interleaved with its MFMAs (scheduling
   // groups below), so the VALU work of one step overlaps the matrix work of the step before.
   auto decode_slot = [&](int slot, half8 (&bb)[SPW]) {
-    const uint32_t* ws = reinterpret_cast<const uint32_t*>(ring + slot * SLOT + BIG_A_U4 + wv * 64);
+    const uint32_t* ws = reinterpret_cast<const uint32_t*>(ring + slot * SLOT + BIG_A_U4 + wv * WREG);
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       uint32_t w[NWW];
@@ -337,7 +353,7 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
     const uint4* sl = ring + slot * SLOT;
     slot = slot + 1 == BIG_D ? 0 : slot + 1;
     // next step's words (the slot of step ks + 1; after the last step a stale slot, decoded unused)
-    const uint32_t* wsn = reinterpret_cast<const uint32_t*>(ring + slot * SLOT + BIG_A_U4 + wv * 64);
+    const uint32_t* wsn = reinterpret_cast<const uint32_t*>(ring + slot * SLOT + BIG_A_U4 + wv * WREG);
     uint32_t wn[SPW][NWW];
 #pragma unroll
     for (int j = 0; j < SPW; ++j)
@@ -409,25 +425,31 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
 // The launch arguments reach it through memory: they are copied into registers first and those
 // loads are complete before the unit's first staging load, so the unit's constant wait counts still
 // count its own staging loads only.
-template <int BITS, int SPW, int NGR>
+template <int BITS, int SPW, int NGR, int RB>
 __device__ __attribute__((noinline)) void unit_f16_big_call(const GemmArgs& a, const int4 t, int nb, int s, int splits,
                                                             int lane, int wv, uint4* ring, uint32_t mask, uint32_t orv) {
   const GemmArgs la = a;
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  unit_f16_big<BITS, SPW, NGR>(la, t, nb, s, splits, lane, wv, ring, mask, orv);
+  unit_f16_big<BITS, SPW, NGR, RB>(la, t, nb, s, splits, lane, wv, ring, mask, orv);
 }
 
-// One unit at the tile's width (BITS = 0: experts of mixed widths 2-4, read from the tile).
+// One unit at the tile's width (BITS = 0 or kMixedWide: experts of mixed widths 2-4 or 2-6, read
+// from the tile).
 template <int BITS, int SPW, int NGR>
 __device__ __forceinline__ void big_unit_width(const GemmArgs& a, const int4 t, int nb, int s, int splits, int lane,
                                                int wv, uint4* ring, uint32_t mask, uint32_t orv) {
-  if constexpr (BITS != 0) {
-    unit_f16_big<BITS, SPW, NGR>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+  constexpr int RB = big_ring_bits<BITS>();
+  if constexpr (BITS != 0 && BITS != kMixedWide) {
+    unit_f16_big<BITS, SPW, NGR, RB>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
   } else {
     const int bits = __builtin_amdgcn_readfirstlane((t.x >> 24) & 0xff);
-    if (bits == 4) unit_f16_big_call<4, SPW, NGR>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
-    else if (bits == 3) unit_f16_big_call<3, SPW, NGR>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
-    else unit_f16_big_call<2, SPW, NGR>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    if (bits == 4) unit_f16_big_call<4, SPW, NGR, RB>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    else if (bits == 3) unit_f16_big_call<3, SPW, NGR, RB>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    else if (BITS == 0 || bits == 2) unit_f16_big_call<2, SPW, NGR, RB>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    else if constexpr (BITS == kMixedWide) {
+      if (bits == 5) unit_f16_big_call<5, SPW, NGR, RB>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+      else unit_f16_big_call<6, SPW, NGR, RB>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    }
   }
 }
 
@@ -439,7 +461,7 @@ __device__ __forceinline__ void big_unit_width(const GemmArgs& a, const int4 t, 
 // bound on the tile count), so this is a permutation of the grid; surplus workgroups leave at once.
 template <int BITS, int SPW, int FC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPW >= 4 ? 2 : 3, 8))) void k_gemm_f16_big(GemmArgs a) {
-  __shared__ uint4 ring[BIG_D * big_slot_u4<SPW>()];
+  __shared__ uint4 ring[BIG_D * big_slot_u4<SPW, big_ring_bits<BITS>()>()];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, kept in an SGPR
   const int NB = a.N / (64 * SPW);
@@ -865,24 +887,15 @@ void launch_f8(const GemmArgs& a, int mg, dim3 grid, hipStream_t s) {
   else hipLaunchKernelGGL((k_gemm_f8<BITS, 1, FC>), grid, dim3(256), 0, s, a);
 }
 
-// Widths 5 and 6 (uniform, or in a mixed set) run only the per-wavefront kernels (tiles of up to
-// 64 rows); the host never asks for 128-row tiles then.
-template <int BITS, int FC>
-void launch_f16_narrow(const GemmArgs& a, int mg, dim3 grid, hipStream_t s) {
-  if (mg >= 4) hipLaunchKernelGGL((k_gemm_f16<BITS, 4, FC>), grid, dim3(256), 0, s, a);
-  else if (mg == 2) hipLaunchKernelGGL((k_gemm_f16<BITS, 2, FC>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_gemm_f16_small<BITS, 1, FC>), grid, dim3(256), 0, s, a);
-}
-
 template <int FC>
 void launch_f16_bits(const GemmArgs& a, int bits, int mg, dim3 grid, hipStream_t s) {
   switch (bits) {
     case 4: launch_f16<4, FC>(a, mg, grid, s); break;
     case 3: launch_f16<3, FC>(a, mg, grid, s); break;
     case 2: launch_f16<2, FC>(a, mg, grid, s); break;
-    case 5: launch_f16_narrow<5, FC>(a, mg, grid, s); break;
-    case 6: launch_f16_narrow<6, FC>(a, mg, grid, s); break;
-    case kMixedWide: launch_f16_narrow<kMixedWide, FC>(a, mg, grid, s); break;
+    case 5: launch_f16<5, FC>(a, mg, grid, s); break;
+    case 6: launch_f16<6, FC>(a, mg, grid, s); break;
+    case kMixedWide: launch_f16<kMixedWide, FC>(a, mg, grid, s); break;
     default: launch_f16<0, FC>(a, mg, grid, s); break;
   }
 }

@@ -197,7 +197,7 @@ void half_planes(int mg, const GemmShape (&sh)[2], bool atomic_fc2, bool (&half)
 // FC1's workgroup tile width for 128-row tiles (both GEMMs' widths must be multiples of 128, as
 // they share the tile list), or 0.
 int big_cols(const tmoe_plan_s* p, bool fp8) {
-  if (fp8 || p->max_bits > 4) return 0;      // 128-row tiles: widths 2-4 only
+  if (fp8) return 0;                          // 128-row tiles: the fp16 GEMMs only
   if (p->H % 128 != 0 || (2 * p->I) % 128 != 0) return 0;
   return (2 * p->I) % 256 == 0 ? 256 : 128;
 }
@@ -547,7 +547,7 @@ tmoe_status linear_forward(const tmoe_linear_plan_s* p, const void* x, int32_t T
       !aligned(wt->su, 2) || !aligned(wt->sv, 2))
     return TMOE_ERR_ALIGNMENT;
 
-  const int mg = p->bits > 4 ? std::min(linear_mg(T, p->N), 4) : linear_mg(T, p->N);   // 128-row tiles: widths 2-4
+  const int mg = linear_mg(T, p->N);
   const int rows = tile_rows(mg);
   const bool big = mg >= 8;
   const int ntiles = (T + rows - 1) / rows;
@@ -670,7 +670,7 @@ tmoe_status tmoe_plan(const tmoe_config* cfg, tmoe_plan_t* out, size_t* scratch_
   p->routes_max = rmax;
   p->max_tiles = static_cast<int>(rmax / p->block_m + p->E + 1);
   p->max_gtiles = static_cast<int>(rmax / 16 + p->E + 1);
-  // W4A8 decodes widths 2-4 only (its kernel reads one two-word window per group of eight)
+  // W4A8 decodes widths 2-4 only (its LDS ring holds one step of 4-bit tiles)
   p->max_bits = *std::max_element(p->bits.begin(), p->bits.end());
   p->fp8_ok = (p->H % 128 == 0) && (p->I % 128 == 0) && p->max_bits <= 4;
   p->uniform_bits = p->bits[0];
