@@ -343,7 +343,7 @@ def cpu_baseline(inp, budget_s: float = 15.0):
     while True:
         y = oracle_np.forward(inp, mode="w4a8" if inp.name == "w4a8" else "w4a16", nthreads=cores)
         runs += 1
-        if time.perf_counter() - t0 >= budget_s or runs >= 20:
+        if time.perf_counter() - t0 >= budget_s or runs >= 60:
             break
     el = time.perf_counter() - t0
     # one forward on a single thread, for the per-core figure
