@@ -66,9 +66,10 @@ __device__ int4 block_exclusive_scan4(int4 v, int4* smem, int4* total) {
 }  // namespace
 
 // Per-expert prefix sums kept in LDS while the tile tables are written: slots, block_m tiles, GEMM
-// tiles and payload bit offsets, each with its total in entry E.
+// tiles of the first and of the second class (see publish_tables) and payload bit offsets, each
+// with its total in entry E.
 struct TableSmem {
-  int off[kMaxExperts + 1], toff[kMaxExperts + 1], goff[kMaxExperts + 1], boff[kMaxExperts + 1];
+  int off[kMaxExperts + 1], toff[kMaxExperts + 1], goff[kMaxExperts + 1], loff[kMaxExperts + 1], boff[kMaxExperts + 1];
 };
 
 // The expert whose range [tab[e], tab[e + 1]) holds i, for 0 <= i < tab[E]: the last e with
@@ -88,6 +89,10 @@ __device__ __forceinline__ int owner_of(const int* tab, int E, int i) {
 // offset (0 for threads past E). With COOP the tile tables are written by all threads, one tile each
 // in turn (large batches, where one expert may hold hundreds of tiles); otherwise each expert's
 // thread writes its own few tiles.
+// GEMM tiles of 128 rows come in two classes: those of more than 64 rows (the GEMM computes all
+// eight 16-row groups) and those of at most 64 rows (four groups, half the work). The list holds
+// the first class, then the second, each in expert order: a launch deals its units in list order,
+// so its last round, which runs on a partly idle chip, takes the short units.
 template <bool COOP>
 __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4* scan_smem, TableSmem& tb) {
   const int tid = threadIdx.x, E = a.num_experts;
@@ -95,14 +100,21 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
   const int bits_e = own ? static_cast<int>((a.packed_bits[tid >> 3] >> (4 * (tid & 7))) & 15u) : 0;
   const int tiles_e = own ? (total_e + a.block_m - 1) / a.block_m : 0;
   const int gtiles_e = own ? (total_e + a.gemm_rows - 1) / a.gemm_rows : 0;
+  const int rem_e = total_e % a.gemm_rows;
+  const int short_e = own && a.gemm_rows == 128 && rem_e > 0 && rem_e <= 64 ? 1 : 0;   // second-class tiles
+  const int long_e = gtiles_e - short_e;                                                // first-class tiles
+  // the payload bit offsets (< 2^13: widths <= 6, E <= 512) share a scan lane with the short tiles
   int4 totals;
-  const int4 offs = block_exclusive_scan4(make_int4(own ? total_e : 0, tiles_e, gtiles_e, bits_e), scan_smem, &totals);
+  const int4 offs = block_exclusive_scan4(make_int4(own ? total_e : 0, tiles_e, long_e, bits_e | (short_e << 16)),
+                                          scan_smem, &totals);
   const int off_e = offs.x;
+  const int boff_e = offs.w & 0xffff, soff_e = offs.w >> 16;
+  const int nlong = totals.z, nbits = totals.w & 0xffff, nshort = totals.w >> 16;
   if (own) {
     a.counts[tid] = total_e;
     a.offsets[tid] = off_e;
     ExpertInfo info;
-    info.word_offset = static_cast<long long>(offs.w) * a.words_per_bit;
+    info.word_offset = static_cast<long long>(boff_e) * a.words_per_bit;
     info.bits = bits_e;
     info.pad = 0;
     a.einfo[tid] = info;
@@ -110,7 +122,8 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
       tb.off[tid] = off_e;
       tb.toff[tid] = offs.y;
       tb.goff[tid] = offs.z;
-      tb.boff[tid] = offs.w;
+      tb.loff[tid] = soff_e;
+      tb.boff[tid] = boff_e;
     } else {
       for (int t = 0; t < tiles_e; ++t) {
         a.tile_expert[offs.y + t] = tid;
@@ -123,7 +136,7 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
         g.y = off_e + t * a.gemm_rows;
         g.z = min(a.gemm_rows, total_e - t * a.gemm_rows);
         g.w = static_cast<int>(info.word_offset >> 8);   // expert regions start on 256-word multiples
-        a.gtiles[offs.z + t] = g;
+        a.gtiles[t < long_e ? offs.z + t : nlong + soff_e] = g;
       }
     }
   }
@@ -131,12 +144,13 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
     if constexpr (COOP) {
       tb.off[E] = totals.x;
       tb.toff[E] = totals.y;
-      tb.goff[E] = totals.z;
-      tb.boff[E] = totals.w;
+      tb.goff[E] = nlong;
+      tb.loff[E] = nshort;
+      tb.boff[E] = nbits;
     }
     a.offsets[E] = totals.x;
     *a.num_tiles = totals.y;
-    *a.num_gtiles = totals.z;
+    *a.num_gtiles = nlong + nshort;
     a.splits[0] = a.nsplit[0];
     a.splits[1] = a.nsplit[1];
     if (a.half) {
@@ -157,9 +171,10 @@ __device__ int publish_tables(const RouteMapArgs& a, int total_e, int bad, int4*
     a.tile_row0[i] = tb.off[e] + t * a.block_m;
     a.tile_rows[i] = min(a.block_m, cnt_e - t * a.block_m);
   }
-  for (int i = tid; i < totals.z; i += blockDim.x) {
-    const int e = owner_of(tb.goff, E, i);
-    const int t = i - tb.goff[e];
+  for (int i = tid; i < nlong + nshort; i += blockDim.x) {
+    // first class: tile i - goff[e] of its expert; second class: the expert's last tile
+    const int e = i < nlong ? owner_of(tb.goff, E, i) : owner_of(tb.loff, E, i - nlong);
+    const int t = i < nlong ? i - tb.goff[e] : tb.goff[e + 1] - tb.goff[e];
     const int cnt_e = tb.off[e + 1] - tb.off[e];
     const int b = tb.boff[e + 1] - tb.boff[e];
     int4 g;
