@@ -321,6 +321,14 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
   for (int g = 0; g < NGR; ++g)
 #pragma unroll
     for (int j = 0; j < SPW; ++j) acc[g][j] = f4{0.f, 0.f, 0.f, 0.f};
+  // one K split: the channel scales of the epilogue are read now, so their latency passes during
+  // the K loop (they are older than every staging load, so the constant wait counts still hold)
+  uint16_t sc16[SPW];
+  if (a.out16) {
+    const uint16_t* cs = a.oscale + static_cast<size_t>(t.x & 0xffffff) * a.N + nt0 * 16 + col;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) sc16[j] = cs[16 * j];
+  }
 
 #pragma unroll
   for (int d = 0; d < BIG_D - 1; ++d) issue(min(ks0 + d, last), d);
@@ -390,10 +398,9 @@ __device__ __forceinline__ void unit_f16_big(const GemmArgs& a, const int4 t, in
   asm volatile("" : "+v"(lane_off));
   if (a.out16) {
     // one K split: the finished sums times the expert's channel scale, rounded once to fp16
-    const uint16_t* cs = a.oscale + static_cast<size_t>(t.x & 0xffffff) * a.N + nt0 * 16 + col;
     float sc[SPW];
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) sc[j] = h2f(cs[16 * j]);
+    for (int j = 0; j < SPW; ++j) sc[j] = h2f(sc16[j]);
     _Float16* o = reinterpret_cast<_Float16*>(a.out16) + static_cast<size_t>(row0) * a.N + nt0 * 16 + col;
 #pragma unroll
     for (int g = 0; g < NGR; ++g)
@@ -465,19 +472,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPW >= 4 ? 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, kept in an SGPR
   const int NB = a.N / (64 * SPW);
-  const int ntiles = *a.num_gtiles;
   const int splits = a.nsplit;
-  const int units = ntiles * NB * splits;
   const int G = gridDim.x;
   const int upt = NB * splits;                              // units of one tile
   const int gi = blockIdx.x >> 3;
   const int first = ((blockIdx.x & 7) + 8 * (gi / upt)) * upt + gi % upt;
+  // each unit's tile entry is read before the loop test, the first one beside the tile count
+  // (an entry past the count is read but never used)
+  int4 t = a.gtiles[min(first / upt, a.max_gtiles - 1)];
+  int ntiles = *a.num_gtiles;
+  t = make_int4(__builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y),
+                __builtin_amdgcn_readfirstlane(t.z), __builtin_amdgcn_readfirstlane(t.w));
+  ntiles = __builtin_amdgcn_readfirstlane(ntiles);
+  asm volatile("" : "+s"(t.x), "+s"(t.y), "+s"(t.z), "+s"(t.w), "+s"(ntiles));   // both loads in flight together
+  const int units = ntiles * NB * splits;
   const uint32_t mask = vreg_const(kMcgMask), orv = kMcgOr;
-  for (int u = first; u < units; u += G) {
+  for (int u = first; u < units; u += G, t = a.gtiles[min(u / upt, a.max_gtiles - 1)]) {
     const int s = u % splits;
     const int rest = u / splits;
     const int nb = rest % NB;
-    const int4 t = a.gtiles[rest / NB];
     if (__builtin_amdgcn_readfirstlane(t.z) > 64) big_unit_width<BITS, SPW, 8>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
     else big_unit_width<BITS, SPW, 4>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
   }
@@ -642,13 +655,18 @@ __global__ __launch_bounds__(256) void k_gemm_f8(GemmArgs a) {
   const int W = gridDim.x * 4;
   const int NG = a.N / (16 * NS);
   const int splits = a.nsplit;
-  const int units = *a.num_gtiles * NG * splits;
+  int4 t = a.gtiles[min(gw / (NG * splits), a.max_gtiles - 1)];   // read beside the tile count
+  int ntiles = *a.num_gtiles;
+  t = make_int4(__builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y),
+                __builtin_amdgcn_readfirstlane(t.z), __builtin_amdgcn_readfirstlane(t.w));
+  ntiles = __builtin_amdgcn_readfirstlane(ntiles);
+  asm volatile("" : "+s"(t.x), "+s"(t.y), "+s"(t.z), "+s"(t.w), "+s"(ntiles));   // both loads in flight together
+  const int units = ntiles * NG * splits;
   const uint32_t mask = vreg_const(kMcgMask), orv = kMcgOr;
-  for (int u = gw; u < units; u += W) {
+  for (int u = gw; u < units; u += W, t = a.gtiles[min(u / (NG * splits), a.max_gtiles - 1)]) {
     const int s = u % splits;
     const int rest = u / splits;
     const int ng = rest % NG;
-    const int4 t = a.gtiles[rest / NG];
     if constexpr (BITS != 0) {
       unit_f8<BITS, MG>(a, t, ng, s, splits, lane, ring, mask, orv);
     } else {

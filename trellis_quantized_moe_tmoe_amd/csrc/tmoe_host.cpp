@@ -391,6 +391,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   g1.out = z;
   g1.gtiles = at<int4>(scratch, p->lay.gtiles);
   g1.num_gtiles = at<int32_t>(scratch, p->lay.scalars) + 2;
+  g1.max_gtiles = p->max_gtiles;
   g1.K = p->H;
   g1.N = 2 * p->I;
   g1.lda = fp16_pitch(p->H);
@@ -594,6 +595,7 @@ tmoe_status linear_forward(const tmoe_linear_plan_s* p, const void* x, int32_t T
   g.out = at<float>(scratch, p->z);
   g.gtiles = lp.gtiles;
   g.num_gtiles = lp.num_gtiles;
+  g.max_gtiles = p->max_gtiles;
   g.nsplit = splits;
   g.K = p->K;
   g.N = p->N;

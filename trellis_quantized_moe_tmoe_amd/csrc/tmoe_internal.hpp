@@ -109,6 +109,7 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
   const uint16_t* oscale = nullptr;  //   out * oscale[e][n] (the channel scale, [E][N]), rounded once
   const int4* gtiles;
   const int32_t* num_gtiles;
+  int max_gtiles = 1;        // entries the tile list has room for
   int nsplit;                // K splits of this GEMM (the host's choice, also published in splits[])
   int K, N;
   int lda;                   // fp16 A row pitch in elements (the fp8 kernels use K)
