@@ -117,6 +117,14 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
   for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) acc[mg][ns] = f4{0.f, 0.f, 0.f, 0.f};
+  // one K split: the epilogue's channel scales, read before the staging loads (older than all of
+  // them, so the constant wait counts still hold)
+  uint16_t sc16[NS];
+  if (a.out16) {
+    const uint16_t* cs = a.oscale + static_cast<size_t>(t.x & 0xffffff) * a.N + nt0 * 16 + col;
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) sc16[ns] = cs[16 * ns];
+  }
 
   auto issue = [&](int ks, int d) {
     uint32_t* slot = ring + d * STAGE;
@@ -171,6 +179,25 @@ __device__ __forceinline__ void unit_f16(const GemmArgs& a, const int4 t, int ng
     if (base + d < ks1) step(d, ks1 - 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // no load may still target the ring
 
+  if (a.out16) {
+    // one K split: the finished sums times the expert's channel scale, rounded once to fp16
+    float sc[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) sc[ns] = h2f(sc16[ns]);
+    _Float16* o16 = reinterpret_cast<_Float16*>(a.out16) + static_cast<size_t>(row0) * a.N + nt0 * 16 + col;
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mg + 4 * grp + i;
+        if (r < rows) {
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns)
+            o16[static_cast<size_t>(r) * a.N + 16 * ns] = static_cast<_Float16>(acc[mg][ns][i] * sc[ns]);
+        }
+      }
+    return;
+  }
   float* o = a.out + (static_cast<size_t>(s) * a.routes + row0) * a.N + nt0 * 16 + col;
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg)

@@ -56,12 +56,23 @@ int choose_splits(long long routes, int ksteps) {
   return 1;
 }
 
+// Extra K splits for wavefront tiles of batches past 512 routes: doubled while the units would
+// leave the persistent wavefronts idle, each unit keeping at least 8 K steps.
+int fill_splits(long long units_per_split, int ksteps) {
+  int s = 1;
+  while (s < 8 && units_per_split * s < kGemmWaveCap && ksteps % (2 * s) == 0 && ksteps / (2 * s) >= 8) s *= 2;
+  return s;
+}
+
 // GEMM tile shape code: 1, 2, 4 = 16-row groups per wavefront tile (64 columns); 8, 16 = workgroup
 // tiles of 128 rows by 128 or 256 columns for large batches (fp16 path; `big_cols` is the widest
-// workgroup tile both output widths are multiples of, or 0).
+// workgroup tile both output widths are multiples of, or 0). Batches of at most 64 rows per expert
+// on average take 64-row wavefront tiles: a 128-row workgroup tile would compute half its rows only,
+// and the wavefront kernel's K splits keep the chip filled (wide geometry at T = 512: FC1 93 -> 73 us).
 int choose_mg(long long routes, int experts, int big_cols) {
   if (routes <= 2LL * experts) return 1;
   if (routes <= 8LL * experts) return 2;
+  if (routes <= 64LL * experts) return 4;
   if (big_cols == 256) return 16;
   if (big_cols == 128) return 8;
   return 4;
@@ -87,6 +98,7 @@ struct tmoe_plan_s {
   std::vector<long long> offsets;   // word offset per expert, [E+1]
   uint32_t packed_bits[64];      // 4 bits per expert: its width
   long long routes_max;
+  long long zrows, vrows;           // rows of the FC1 / FC2 output area (split planes included)
   int max_tiles, max_gtiles;
   bool fp8_ok;
   int uniform_bits;                 // the width shared by all experts; 0 (mixed 2-4) or kMixedWide
@@ -122,11 +134,18 @@ void build_layout(tmoe_plan_s* p) {
   L.gtiles = take(16ull * p->max_gtiles);
   L.wgc = take(4ull * ((R + kRouteChunk - 1) / kRouteChunk) * (p->E + 1));   // per-workgroup route counts
   L.a1 = take(2ull * R * fp16_pitch(p->H));           // fp16 (padded rows), or E4M3 + E8M0 planes
-  const long long zrows = max_split_rows(R, p->H / 32, p->H / 128 > 0 ? p->H / 128 : 1);
+  // the extra splits of 64-row wavefront tiles, sized at the largest batch (smaller batches take no
+  // more splits than fit: the GEMM shape clamps them)
+  const long long gt64 = std::min<long long>(R, p->E + R / 64 + 1);
+  const long long zrows = std::max(max_split_rows(R, p->H / 32, p->H / 128 > 0 ? p->H / 128 : 1),
+                                   R * fill_splits(gt64 * (2 * p->I / 64), p->H / 32));
   L.z = take(4ull * zrows * 2 * p->I);
   L.b = take(2ull * R * fp16_pitch(p->I));
-  const long long vrows = max_split_rows(R, p->I / 32, p->I / 128 > 0 ? p->I / 128 : 1);
+  const long long vrows = std::max(max_split_rows(R, p->I / 32, p->I / 128 > 0 ? p->I / 128 : 1),
+                                   R * fill_splits(gt64 * (p->H / 64), p->I / 32));
   L.v = take(4ull * vrows * p->H);
+  p->zrows = zrows;
+  p->vrows = vrows;
   L.total = off;
 }
 
@@ -178,6 +197,11 @@ GemmShape gemm_shape(const tmoe_plan_s* p, long long R, int mg_in, bool fp8, int
   g.ksteps = K / (fp8 ? 128 : 32);
   g.most = choose_splits(R, g.ksteps);
   const long long gt_ub = std::min<long long>(R, p->E + R / gemm_rows + 1);
+  if (!big && R > 512) {
+    g.most = std::max(g.most, fill_splits(gt_ub * g.ng, g.ksteps));
+    const long long cap = fc == 1 ? p->zrows : p->vrows;
+    while (g.most > 1 && R * g.most > cap) g.most /= 2;
+  }
   g.waves = static_cast<int>(std::min<long long>(big ? kGemmGroupCap : kGemmWaveCap, gt_ub * g.ng * g.most));
   if (big) {                                    // a whole number of 8-tile rounds of units
     const int per = 8 * g.ng * g.most;
@@ -186,12 +210,12 @@ GemmShape gemm_shape(const tmoe_plan_s* p, long long R, int mg_in, bool fp8, int
   return g;
 }
 
-// GEMMs on 128-row tiles with one K split finish their sums in one launch: they apply the channel
-// scale in the epilogue and leave one fp16 plane, half the bytes of fp32 for the next launch to read.
-// The opt-in atomic FC2 adds into y instead of leaving v.
-void half_planes(int mg, const GemmShape (&sh)[2], bool atomic_fc2, bool (&half)[2]) {
-  half[0] = mg >= 8 && sh[0].most == 1;
-  half[1] = mg >= 8 && sh[1].most == 1 && !atomic_fc2;
+// fp16 GEMMs with one K split finish their sums in one launch: they apply the channel scale in the
+// epilogue and leave one fp16 plane, half the bytes of fp32 for the next launch to read. The opt-in
+// atomic FC2 adds into y instead of leaving v.
+void half_planes(bool fp8, const GemmShape (&sh)[2], bool atomic_fc2, bool (&half)[2]) {
+  half[0] = !fp8 && sh[0].most == 1;
+  half[1] = !fp8 && sh[1].most == 1 && !atomic_fc2;
 }
 
 // FC1's workgroup tile width for 128-row tiles (both GEMMs' widths must be multiples of 128, as
@@ -351,7 +375,7 @@ tmoe_status forward(tmoe_plan_t p, const void* x, const void* ids, const float* 
   // the FP32-atomic FC2 reduction adds into y, which the activation launch zeroes beforehand
   const bool atomic_fc2 = p->fc2_reduce == TMOE_FC2_ATOMIC && fc2_atomic_fits(p, fp8);
   bool half[2];
-  half_planes(mg, sh, atomic_fc2, half);
+  half_planes(fp8, sh, atomic_fc2, half);
 
   const int32_t* sorted = at<int32_t>(scratch, p->lay.sorted);
   const int32_t* slot_expert = at<int32_t>(scratch, p->lay.slot_e);
@@ -717,7 +741,7 @@ tmoe_status tmoe_build_route_map(tmoe_plan_t p, const void* ids, int32_t T, void
   const int gemm_rows = tile_rows(mg);
   const GemmShape sh[2] = {gemm_shape(p, R, mg, false, 1), gemm_shape(p, R, mg, false, 2)};
   bool half[2];
-  half_planes(mg, sh, p->fc2_reduce == TMOE_FC2_ATOMIC && fc2_atomic_fits(p, false), half);
+  half_planes(false, sh, p->fc2_reduce == TMOE_FC2_ATOMIC && fc2_atomic_fits(p, false), half);
   (void)hipGetLastError();
   enqueue_route_map(p, ids, T, gemm_rows, sh, half, scratch, nullptr, false, static_cast<hipStream_t>(stream));
   *view = make_view(p, scratch);

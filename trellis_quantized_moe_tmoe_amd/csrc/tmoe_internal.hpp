@@ -105,7 +105,7 @@ struct GemmArgs {            // out[s][slot][n] = sum over k in split s of A[slo
   const int32_t* arow;       // operand row of each slot (FC1: the slot's route), or null: row = slot
   const uint8_t* a_scale;    // [R][K/32] (fp8 only)
   float* out;                // [splits][R][N]
-  uint16_t* out16 = nullptr; // 128-row tiles with one K split may instead leave fp16 [R][N] of
+  uint16_t* out16 = nullptr; // fp16 GEMMs with one K split may instead leave fp16 [R][N] of
   const uint16_t* oscale = nullptr;  //   out * oscale[e][n] (the channel scale, [E][N]), rounded once
   const int4* gtiles;
   const int32_t* num_gtiles;
