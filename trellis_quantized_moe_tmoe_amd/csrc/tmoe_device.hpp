@@ -214,8 +214,14 @@ __device__ __forceinline__ float h2f(uint16_t h) {
 // A row segment of 64*EPL values lives in a wavefront with element e = i*64 + lane in v[i].
 // The butterflies of the Walsh-Hadamard transform in natural order commute, so the cross-lane
 // strides 1..32 and the in-register strides 64..32*EPL can run in any order. Cross-lane partners
-// come from DPP (strides 1, 2, 8), ds_swizzle (4, 16) and one lane permute (32); the butterfly is
-// then new = partner + sign * own with sign = -1 on the lane holding the upper element.
+// come from DPP (strides 1, 2, 8), ds_swizzle (4, 16) and one lane permute (32). A lane stage
+// computes own + sign * partner (sign = -1 on the lane holding the upper element), which is the
+// butterfly's lower output on the lower lane and the negated upper output on the upper lane; the
+// partner is the multiplicand, so a DPP partner folds into the fused multiply-add (one instruction
+// per value). After the six lane stages lane l holds (-1)^popcount(l) times its true values (a sign
+// that passes unchanged through the in-register stages, which are linear), and the final scale
+// carries that sign. Every value has the same bits as the plain butterflies give: each add or
+// subtract is the same one, up to an exact negation.
 template <int S>
 __device__ __forceinline__ float lane_partner(float v) {
   const int x = __float_as_int(v);
@@ -229,14 +235,62 @@ __device__ __forceinline__ float lane_partner(float v) {
   return __int_as_float(r);
 }
 
+// v[i] += (v[i] of the DPP partner lane) * sg for N values, one v_fmac_f32 with a DPP source each
+// (the compiler keeps the DPP move separate). The leading s_nop gives the two wait states a DPP read
+// needs after a VALU write of its source register; every source is written before the statement.
+#define TMOE_FMAC_DPP(I, N, CTRL) "v_fmac_f32_dpp %" #I ", %" #I ", %" #N " " CTRL " row_mask:0xf bank_mask:0xf\n"
+#define TMOE_DPP_STAGE(CTRL)                                                                             \
+  do {                                                                                                   \
+    if constexpr (N == 8) {                                                                              \
+      asm("s_nop 1\n" TMOE_FMAC_DPP(0, 8, CTRL) TMOE_FMAC_DPP(1, 8, CTRL) TMOE_FMAC_DPP(2, 8, CTRL)      \
+              TMOE_FMAC_DPP(3, 8, CTRL) TMOE_FMAC_DPP(4, 8, CTRL) TMOE_FMAC_DPP(5, 8, CTRL)              \
+                  TMOE_FMAC_DPP(6, 8, CTRL) TMOE_FMAC_DPP(7, 8, CTRL)                                    \
+          : "+v"(v[B]), "+v"(v[B + 1]), "+v"(v[B + 2]), "+v"(v[B + 3]), "+v"(v[B + 4]), "+v"(v[B + 5]), \
+            "+v"(v[B + 6]), "+v"(v[B + 7])                                                               \
+          : "v"(sg));                                                                                    \
+    } else if constexpr (N == 4) {                                                                       \
+      asm("s_nop 1\n" TMOE_FMAC_DPP(0, 4, CTRL) TMOE_FMAC_DPP(1, 4, CTRL) TMOE_FMAC_DPP(2, 4, CTRL)      \
+              TMOE_FMAC_DPP(3, 4, CTRL)                                                                  \
+          : "+v"(v[B]), "+v"(v[B + 1]), "+v"(v[B + 2]), "+v"(v[B + 3])                                   \
+          : "v"(sg));                                                                                    \
+    } else if constexpr (N == 2) {                                                                       \
+      asm("s_nop 1\n" TMOE_FMAC_DPP(0, 2, CTRL) TMOE_FMAC_DPP(1, 2, CTRL) : "+v"(v[B]), "+v"(v[B + 1]) \
+          : "v"(sg));                                                                                    \
+    } else {                                                                                             \
+      asm("s_nop 1\n" TMOE_FMAC_DPP(0, 1, CTRL) : "+v"(v[B]) : "v"(sg));                                \
+    }                                                                                                    \
+  } while (0)
+
+template <int S, int B, int N, int EPL>
+__device__ __forceinline__ void fmac_dpp(float (&v)[EPL], float sg) {
+  if constexpr (S == 1) TMOE_DPP_STAGE("quad_perm:[1,0,3,2]");
+  else if constexpr (S == 2) TMOE_DPP_STAGE("quad_perm:[2,3,0,1]");
+  else TMOE_DPP_STAGE("row_ror:8");
+}
+#undef TMOE_DPP_STAGE
+#undef TMOE_FMAC_DPP
+
+template <int S, int EPL, int B = 0>
+__device__ __forceinline__ void fmac_dpp_all(float (&v)[EPL], float sg) {
+  if constexpr (B < EPL) {
+    constexpr int N = EPL - B >= 8 ? 8 : EPL - B;
+    fmac_dpp<S, B, N>(v, sg);
+    fmac_dpp_all<S, EPL, B + N>(v, sg);
+  }
+}
+
 template <int S, int EPL>
 __device__ __forceinline__ void fwht_lane_stage(float (&v)[EPL], int lane) {
   const float sg = (lane & S) ? -1.0f : 1.0f;
-  float p[EPL];
+  if constexpr (S == 1 || S == 2 || S == 8) {
+    fmac_dpp_all<S>(v, sg);
+  } else {
+    float p[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) p[i] = lane_partner<S>(v[i]);
+    for (int i = 0; i < EPL; ++i) p[i] = lane_partner<S>(v[i]);
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) v[i] = fmaf(sg, v[i], p[i]);
+    for (int i = 0; i < EPL; ++i) v[i] = fmaf(p[i], sg, v[i]);
+  }
 }
 
 template <int EPL>
@@ -263,8 +317,9 @@ __device__ __forceinline__ void fwht_segment(float (&v)[EPL], int lane) {
                          : (EPL == 4) ? 0.0625f : (EPL == 8) ? 0.04419417382415922f
                          : (EPL == 16) ? 0.03125f : (EPL == 32) ? 0.02209708691207961f
                          : 0.015625f;
+  const float fs = (__builtin_popcount(lane & 63) & 1) ? -kScale : kScale;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) v[i] *= kScale;
+  for (int i = 0; i < EPL; ++i) v[i] *= fs;
 }
 
 // ------------------------------------------------------------------ MXFP8
