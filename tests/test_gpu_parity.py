@@ -138,6 +138,51 @@ def test_rotation_kernel(n):
     assert np.max(np.abs(got - want)) <= 1e-5 * np.max(np.abs(want))
 
 
+def _wavefront_fwht_f32(x):
+    """float32 emulation of the wavefront transform's arithmetic on rows held strided (element
+    off + 64 i + lane in value i of the lane): segments of 64 S values (the whole row for a power of
+    two, else 128-blocks and a 64-value tail); lane stages at strides 1, 2, 4, 8, 16, 32 compute
+    own + sign * partner (sign -1 on the lane with the stride's bit set), rounded once; in-register
+    stages a + b, a - b; then a multiply by (-1)^popcount(lane) / sqrt(64 S) as an fp32 constant."""
+    scale = {1: 0.125, 2: 0.08838834764831845, 4: 0.0625, 8: 0.04419417382415922, 16: 0.03125,
+             32: 0.02209708691207961, 64: 0.015625}
+    rows, n = x.shape
+    out = x.astype(np.float32).copy()
+    pow2 = n & (n - 1) == 0
+    segs = [(0, n)] if pow2 else [(o, 128) for o in range(0, n - n % 128, 128)] + ([(n - 64, 64)] if n % 128 else [])
+    lane = np.arange(64)
+    sign_of = {s: np.where(lane & s, np.float32(-1), np.float32(1)) for s in (1, 2, 4, 8, 16, 32)}
+    parity = np.array([bin(l).count("1") & 1 for l in lane])
+    for off, L in segs:
+        S = L // 64
+        v = out[:, off:off + L].reshape(rows, S, 64).copy()         # [row][i][lane]
+        for s in (1, 2, 4, 8, 16, 32):
+            v = v + sign_of[s] * v[:, :, lane ^ s]                  # exact product, one rounding
+        t = 1
+        while t < S:
+            for i in range(S):
+                if i & t == 0:
+                    a, b = v[:, i].copy(), v[:, i | t].copy()
+                    v[:, i], v[:, i | t] = a + b, a - b
+            t <<= 1
+        fs = np.where(parity == 1, -np.float32(scale[S]), np.float32(scale[S])).astype(np.float32)
+        out[:, off:off + L] = (v * fs).reshape(rows, L)
+    return out
+
+
+@pytest.mark.parametrize("n", [64, 128, 256, 512, 1024, 2048, 4096, 320, 2560])
+def test_rotation_kernel_bits(n):
+    """The rotation kernel's bits against a float32 emulation of its own butterfly order (the lane
+    stages' fused DPP multiply-adds carry the sign of the lower/upper output in the final scale)."""
+    from trellis_quantized_moe_tmoe_amd.layer import debug_rotate
+    rng = np.random.default_rng(100 + n)
+    x = rng.standard_normal((37, n)).astype(np.float32)
+    say(f"[case] rotation bits n={n}")
+    got = debug_rotate(torch.from_numpy(x).cuda()).cpu().numpy()
+    want = _wavefront_fwht_f32(x)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
 @pytest.mark.parametrize("name,T", [c for c in ALL_CASES if c[0] != "w4a8"])
 def test_layer_w4a16(name, T):
     c = Case(name, T)
