@@ -504,9 +504,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPW >= 4 ? 
   const int upt = NB * splits;                              // units of one tile
   const int gi = blockIdx.x >> 3;
   const int first = ((blockIdx.x & 7) + 8 * (gi / upt)) * upt + gi % upt;
-  // each unit's tile entry is read before the loop test, the first one beside the tile count
-  // (an entry past the count is read but never used)
-  int4 t = a.gtiles[min(first / upt, a.max_gtiles - 1)];
+  // The first unit's tile entry is read beside the tile count; every later unit's entry is a scalar
+  // load issued when the unit before it starts, so it has landed when that unit ends (the tile list
+  // is written by an earlier launch and only read here; an entry past the count is read but never
+  // used).
+  typedef int tile_v __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(4))) tile_v* tiles_ptr;
+  const tiles_ptr gt = reinterpret_cast<tiles_ptr>(reinterpret_cast<uintptr_t>(a.gtiles));
+  auto tile_at = [&](int u) {
+    const tile_v v = gt[min(u / upt, a.max_gtiles - 1)];
+    return make_int4(v.x, v.y, v.z, v.w);
+  };
+  int4 t = tile_at(first);
   int ntiles = *a.num_gtiles;
   t = make_int4(__builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y),
                 __builtin_amdgcn_readfirstlane(t.z), __builtin_amdgcn_readfirstlane(t.w));
@@ -514,12 +523,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPW >= 4 ? 
   asm volatile("" : "+s"(t.x), "+s"(t.y), "+s"(t.z), "+s"(t.w), "+s"(ntiles));   // both loads in flight together
   const int units = ntiles * NB * splits;
   const uint32_t mask = vreg_const(kMcgMask), orv = kMcgOr;
-  for (int u = first; u < units; u += G, t = a.gtiles[min(u / upt, a.max_gtiles - 1)]) {
+  for (int u = first; u < units; u += G) {
+    const int4 tn = tile_at(u + G);
     const int s = u % splits;
     const int rest = u / splits;
     const int nb = rest % NB;
     if (__builtin_amdgcn_readfirstlane(t.z) > 64) big_unit_width<BITS, SPW, 8>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
     else big_unit_width<BITS, SPW, 4>(a, t, nb, s, splits, lane, wv, ring, mask, orv);
+    t = tn;
   }
 }
 
