@@ -24,9 +24,15 @@ FLAGS = [
 ]
 
 
+# Per-source flags. The row kernels' only MFMAs (the activation's 512-point rotations) keep their
+# results in ordinary VGPRs: accumulation registers would cost that kernel occupancy and a copy of
+# every result.
+EXTRA = {"k_rowops.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -209,6 +209,137 @@ struct ActBody {
   }
 };
 
+// ---- 512-point rotations on the matrix cores (rows of I = 512 fp16 values)
+// With element i = 32a + b (a < 16, b < 32) the transform is H_16 (x) H_32: Y[a'][b'] = sum over a, b
+// of H16[a'][a] H32[b'][b] X[a][b]. Four 16x16 MFMA stages carry it, each taking the previous
+// output layout as it stands: a C tile (lane l: rows 4(l/16)+[0,4), column l%16) is a K = 16
+// operand over its rows, as the B operand of the next product or, read as rows = its column, as the
+// A operand; the constant operands absorb the order of the K values. The forward transform of a row
+// in memory contracts b (A = the row, lane l: elements 32(l%16) + 8(l/16) + [0,8)), then a, leaving
+// the "C2" layout: tile h, value i of lane l is element 32(4(l/16)+i) + 16h + l%16. A transform of
+// values in the C2 layout contracts a (A = the C2 tile), then b, leaving tile h, value i of lane l
+// as element 32(l%16) + 16h + 4(l/16) + i. Entries of H are +-1 (exact in fp16); every stage sums
+// in fp32 and hands its output to the next stage rounded once to fp16.
+namespace had512 {
+constexpr uint32_t hbit(int i, int j) { return (__builtin_popcount(i & j) & 1) ? 0xBC00u : 0x3C00u; }
+constexpr int stage4_k(int q, int r) { return r < 4 ? 4 * q + r : 16 + 4 * q + r - 4; }
+// per lane, fp16 pairs: [0, 2) H16[l%16][4(l/16)+r] (A of the a-contraction of the forward
+// transform, B of the second transform's); [2, 10) H32[16h + l%16][8(l/16)+r] for h = 0, 1 (B of
+// the b-contraction of the forward transform); [10, 18) H32[16h + l%16][stage4_k(l/16, r)] (A of the
+// second transform's b-contraction, whose K values arrive as rows 4(l/16)+[0,4) of both C tiles)
+struct Table {
+  uint32_t w[64][20];
+};
+constexpr Table make_table() {
+  Table t{};
+  for (int l = 0; l < 64; ++l) {
+    const int c = l % 16, q = l / 16;
+    for (int pr = 0; pr < 2; ++pr) t.w[l][pr] = hbit(c, 4 * q + 2 * pr) | (hbit(c, 4 * q + 2 * pr + 1) << 16);
+    for (int h = 0; h < 2; ++h)
+      for (int pr = 0; pr < 4; ++pr) {
+        t.w[l][2 + 4 * h + pr] = hbit(16 * h + c, 8 * q + 2 * pr) | (hbit(16 * h + c, 8 * q + 2 * pr + 1) << 16);
+        t.w[l][10 + 4 * h + pr] =
+            hbit(16 * h + c, stage4_k(q, 2 * pr)) | (hbit(16 * h + c, stage4_k(q, 2 * pr + 1)) << 16);
+      }
+  }
+  return t;
+}
+__device__ const Table kTable = make_table();
+
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half4v to_half4(f4 v) {
+  return half4v{static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]), static_cast<_Float16>(v[2]),
+                static_cast<_Float16>(v[3])};
+}
+
+struct Operands {
+  half4v h16;
+  half8 h32b[2], h32a[2];
+};
+
+__device__ __forceinline__ Operands load_operands(int lane) {
+  const u4v* src = reinterpret_cast<const u4v*>(kTable.w[lane]);
+  const u4v w0 = src[0], w1 = src[1], w2 = src[2], w3 = src[3], w4 = src[4];
+  Operands o;
+  o.h16 = __builtin_bit_cast(half4v, u2v{w0[0], w0[1]});
+  o.h32b[0] = __builtin_bit_cast(half8, u4v{w0[2], w0[3], w1[0], w1[1]});
+  o.h32b[1] = __builtin_bit_cast(half8, u4v{w1[2], w1[3], w2[0], w2[1]});
+  o.h32a[0] = __builtin_bit_cast(half8, u4v{w2[2], w2[3], w3[0], w3[1]});
+  o.h32a[1] = __builtin_bit_cast(half8, u4v{w3[2], w3[3], w4[0], w4[1]});
+  return o;
+}
+
+// Forward transform (unscaled) of the row whose A operand the lane holds: out[h] = C2 tile h.
+__device__ __forceinline__ void forward(const Operands& o, half8 x, f4 (&out)[2]) {
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f4 c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, o.h32b[h], z, 0, 0, 0);
+    out[h] = __builtin_amdgcn_mfma_f32_16x16x16f16(o.h16, to_half4(c1), z, 0, 0, 0);
+  }
+}
+
+// Transform (unscaled) of values in the C2 layout: out[h] = tile h of the second transform's layout.
+__device__ __forceinline__ void from_c2(const Operands& o, const f4 (&v)[2], f4 (&out)[2]) {
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  f4 c3[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) c3[h] = __builtin_amdgcn_mfma_f32_16x16x16f16(to_half4(v[h]), o.h16, z, 0, 0, 0);
+  const half4v lo = to_half4(c3[0]), hi = to_half4(c3[1]);
+  const half8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) out[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.h32a[h], b, z, 0, 0, 0);
+}
+}  // namespace had512
+
+// The activation of one slot with I = 512 and one fp16 FC1 plane (scale1 applied), its three
+// rotations on the matrix cores: g and u are forward transforms of the plane's halves, the product
+// is transformed from the C2 layout and stored from the second transform's layout.
+__device__ __forceinline__ void act_row_mfma(const ActArgs& a, int p, int e, int lane) {
+  constexpr int I = 512;
+  constexpr float kScale = 0.04419417382415922f;   // 1/sqrt(512), rounded once to fp32
+  const int c = lane & 15, q = lane >> 4;
+  const _Float16* zr = reinterpret_cast<const _Float16*>(a.z16) + static_cast<size_t>(p) * 2 * I + 32 * c + 8 * q;
+  const half8 xg = *reinterpret_cast<const half8*>(zr);
+  const half8 xu = *reinterpret_cast<const half8*>(zr + I);
+  const had512::Operands o = had512::load_operands(lane);
+  // signs at the C2 positions 32(4q+i) + 16h + c
+  const uint16_t* s1 = a.sv1 + static_cast<size_t>(e) * 2 * I + 128 * q + c;
+  const uint16_t* s2 = a.su2 + static_cast<size_t>(e) * I + 128 * q + c;
+  float sg[2][4], su[2][4], sd[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sg[h][i] = h2f(s1[32 * i + 16 * h]);
+      su[h][i] = h2f(s1[I + 32 * i + 16 * h]);
+      sd[h][i] = h2f(s2[32 * i + 16 * h]);
+    }
+  f4 g[2], u[2], v[2];
+  had512::forward(o, xg, g);
+  had512::forward(o, xu, u);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gg = (g[h][i] * kScale) * sg[h][i];
+      const float uu = (u[h][i] * kScale) * su[h][i];
+      v[h][i] = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * uu * sd[h][i];   // SiLU(g) * u * su2
+    }
+  f4 y[2];
+  had512::from_c2(o, v, y);
+  _Float16* out = static_cast<_Float16*>(a.b) + static_cast<size_t>(p) * a.ldb + 32 * c + 4 * q;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const had512::half4v r = {static_cast<_Float16>(y[h][0] * kScale), static_cast<_Float16>(y[h][1] * kScale),
+                      static_cast<_Float16>(y[h][2] * kScale), static_cast<_Float16>(y[h][3] * kScale)};
+    *reinterpret_cast<had512::half4v*>(out + 16 * h) = r;
+  }
+}
+
 // One wavefront per (slot, row segment): every step of the epilogue (rotations, SiLU, scales) stays
 // inside one segment of the intermediate row.
 template <int EPL, bool MX, int SMAX>
@@ -229,6 +360,12 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
   if (p >= a.routes) return;
   const int e = a.slot_expert[p];                // -1 past the filled slots (dropped routes)
   if (e < 0) return;
+  if constexpr (EPL == 8 && !MX && SMAX == 0) {
+    if (!a.rot.identity) {
+      act_row_mfma(a, p, e, lane);
+      return;
+    }
+  }
   ActBody<MX, SMAX> body{a, lane, p, e, a.rot.n, SMAX};
   run_segment<EPL>(a.rot, seg, body);
 }
