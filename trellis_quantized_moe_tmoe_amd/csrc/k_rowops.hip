@@ -282,6 +282,26 @@ __device__ __forceinline__ void forward(const Operands& o, half8 x, f4 (&out)[2]
   }
 }
 
+// 1024-point transform (unscaled) of a row in memory, H_32 (x) H_32 with element i = 32a + b: x[ha]
+// holds rows a = 16 ha + l%16, elements 8(l/16) + [0,8) of each; out[ha][hb] is the C tile of rows
+// a' = 16 ha + 4(l/16) + [0,4), column b' = 16 hb + l%16 (element 32a' + b').
+__device__ __forceinline__ void forward1024(const Operands& o, const half8 (&x)[2], f4 (&out)[2][2]) {
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  f4 c1[2][2];
+#pragma unroll
+  for (int ha = 0; ha < 2; ++ha)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) c1[ha][hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[ha], o.h32b[hb], z, 0, 0, 0);
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    // K = a over both row tiles: rows 4(l/16)+[0,4) of tile 0, then of tile 1 (the order h32a assumes)
+    const half4v lo = to_half4(c1[0][hb]), hi = to_half4(c1[1][hb]);
+    const half8 bk = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+    for (int ha = 0; ha < 2; ++ha) out[ha][hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.h32a[ha], bk, z, 0, 0, 0);
+  }
+}
+
 // Transform (unscaled) of values in the C2 layout: out[h] = tile h of the second transform's layout.
 __device__ __forceinline__ void from_c2(const Operands& o, const f4 (&v)[2], f4 (&out)[2]) {
   const f4 z = {0.f, 0.f, 0.f, 0.f};
@@ -306,7 +326,12 @@ __device__ __forceinline__ void act_row_mfma(const ActArgs& a, int p, int e, int
   const half8 xg = *reinterpret_cast<const half8*>(zr);
   const half8 xu = *reinterpret_cast<const half8*>(zr + I);
   const had512::Operands o = had512::load_operands(lane);
-  // signs at the C2 positions 32(4q+i) + 16h + c
+  f4 g[2], u[2], v[2];
+  had512::forward(o, xg, g);
+  had512::forward(o, xu, u);
+  // signs at the C2 positions 32(4q+i) + 16h + c, read after the products (held beside the
+  // operands they would cost the kernel a wavefront per SIMD)
+  __builtin_amdgcn_sched_barrier(0);
   const uint16_t* s1 = a.sv1 + static_cast<size_t>(e) * 2 * I + 128 * q + c;
   const uint16_t* s2 = a.su2 + static_cast<size_t>(e) * I + 128 * q + c;
   float sg[2][4], su[2][4], sd[2][4];
@@ -318,9 +343,6 @@ __device__ __forceinline__ void act_row_mfma(const ActArgs& a, int p, int e, int
       su[h][i] = h2f(s1[I + 32 * i + 16 * h]);
       sd[h][i] = h2f(s2[32 * i + 16 * h]);
     }
-  f4 g[2], u[2], v[2];
-  had512::forward(o, xg, g);
-  had512::forward(o, xu, u);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -439,6 +461,38 @@ __global__ __launch_bounds__(EPL >= 64 ? 256 : 1024) void k_combine(CombineArgs 
       if constexpr (split) {
         if (L == 128) in_registers(std::integral_constant<int, 2>{});
         else in_registers(std::integral_constant<int, 1>{});
+      } else if constexpr (EPL == 16 && SMAX == 0) {
+        if (a.rot.identity) {
+          in_registers(std::integral_constant<int, EPL>{});
+        } else {
+          // one fp16 plane (scale2 applied): R_H on the matrix cores, then sign and weight (1/32
+          // folded into the weight exactly) into the route's LDS row at the natural positions
+          const int c = lane & 15, q = lane >> 4;
+          const _Float16* vr = reinterpret_cast<const _Float16*>(a.v16) + static_cast<size_t>(p) * H + 32 * c + 8 * q;
+          const half8 x[2] = {*reinterpret_cast<const half8*>(vr), *reinterpret_cast<const half8*>(vr + 512)};
+          const had512::Operands o = had512::load_operands(lane);
+          f4 y[2][2];
+          had512::forward1024(o, x, y);
+          // the signs are read after the products (held beside the operands they would cost the
+          // kernel a wavefront per SIMD)
+          __builtin_amdgcn_sched_barrier(0);
+          const uint16_t* sg = a.sv2 + static_cast<size_t>(e_r) * H + 128 * q + c;
+          float sv[2][2][4];
+#pragma unroll
+          for (int ha = 0; ha < 2; ++ha)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sv[ha][hb][i] = h2f(sg[512 * ha + 32 * i + 16 * hb]);
+          const float wt = w_r * 0.03125f;
+          float* rr = row + 128 * q + c;
+#pragma unroll
+          for (int ha = 0; ha < 2; ++ha)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) rr[512 * ha + 32 * i + 16 * hb] = wt * (y[ha][hb][i] * sv[ha][hb][i]);
+        }
       } else if constexpr (EPL <= 16) {
         in_registers(std::integral_constant<int, EPL>{});
       } else {
