@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(HERE, "libtmoe.so")
 SOURCES = ["k_route_map.hip", "k_rowops.hip", "k_trellis_gemm.hip", "k_small_arm.hip", "tmoe_host.cpp"]
-HEADERS = ["tmoe_device.hpp", "tmoe_internal.hpp", "tmoe_rowbody.hpp", "tmoe_routemap.hpp"]
+HEADERS = ["tmoe_device.hpp", "tmoe_hadamard.hpp", "tmoe_internal.hpp", "tmoe_rowbody.hpp", "tmoe_routemap.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -24,9 +24,9 @@ FLAGS = [
 ]
 
 
-# Per-source flags. The row kernels' only MFMAs (the activation's 512-point rotations) keep their
-# results in ordinary VGPRs: accumulation registers would cost that kernel occupancy and a copy of
-# every result.
+# Per-source flags. The row kernels' MFMAs (the rotations of rows of 512 and 1024 values in the
+# activation and the combine at large batches) keep their results in ordinary VGPRs: accumulation
+# registers would cost those kernels occupancy and a copy of every result.
 EXTRA = {"k_rowops.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
