@@ -211,50 +211,74 @@ struct ActBody {
 };
 
 
-// The activation of one slot with I = 512 and one fp16 FC1 plane (scale1 applied), its three
-// rotations on the matrix cores: g and u are forward transforms of the plane's halves, the product
-// is transformed from the C2 layout and stored from the second transform's layout.
-__device__ __forceinline__ void act_row_mfma(const ActArgs& a, int p, int e, int lane) {
+// The activation of kActSlots consecutive slots from p0 with I = 512 and one fp16 FC1 plane (scale1
+// applied), their three rotations on the matrix cores: g and u are forward transforms of the plane's
+// halves, the product is transformed from the C2 layout and stored from the second transform's
+// layout. Slots are grouped by expert, so the sign rows are read again only where the expert
+// changes, and the next slot's FC1 row is requested before the current one is transformed. Filled
+// slots are contiguous: the first slot of expert -1 ends the wavefront's work.
+constexpr int kActSlots = 4;
+__device__ __forceinline__ void act_rows_mfma(const ActArgs& a, int p0, int lane) {
   constexpr int I = 512;
   constexpr float kScale = 0.04419417382415922f;   // 1/sqrt(512), rounded once to fp32
   const int c = lane & 15, q = lane >> 4;
-  const _Float16* zr = reinterpret_cast<const _Float16*>(a.z16) + static_cast<size_t>(p) * 2 * I + 32 * c + 8 * q;
-  const half8 xg = *reinterpret_cast<const half8*>(zr);
-  const half8 xu = *reinterpret_cast<const half8*>(zr + I);
+  auto row = [&](int p) {
+    return reinterpret_cast<const _Float16*>(a.z16) + static_cast<size_t>(p) * 2 * I + 32 * c + 8 * q;
+  };
+  int p = p0;
+  int e = a.slot_expert[p];                       // (p0 < routes)
+  if (e < 0) return;
+  half8 xg = *reinterpret_cast<const half8*>(row(p));
+  half8 xu = *reinterpret_cast<const half8*>(row(p) + I);
   const hmfma::Operands o = hmfma::load_operands(lane);
-  f4 g[2], u[2], v[2];
-  hmfma::forward(o, xg, g);
-  hmfma::forward(o, xu, u);
-  // signs at the C2 positions 32(4q+i) + 16h + c, read after the products (held beside the
-  // operands they would cost the kernel a wavefront per SIMD)
-  __builtin_amdgcn_sched_barrier(0);
-  const uint16_t* s1 = a.sv1 + static_cast<size_t>(e) * 2 * I + 128 * q + c;
-  const uint16_t* s2 = a.su2 + static_cast<size_t>(e) * I + 128 * q + c;
   float sg[2][4], su[2][4], sd[2][4];
+  int e_signs = -1;
+  for (int k = 0; k < kActSlots; ++k) {
+    const int pn = p + 1;
+    const bool more = k + 1 < kActSlots && pn < a.routes;
+    const int en = more ? a.slot_expert[pn] : -1;
+    const _Float16* rn = row(more ? pn : p);       // (a repeat of the current row when there is none)
+    const half8 ng = *reinterpret_cast<const half8*>(rn);
+    const half8 nu = *reinterpret_cast<const half8*>(rn + I);
+    f4 g[2], u[2], v[2];
+    hmfma::forward(o, xg, g);
+    hmfma::forward(o, xu, u);
+    if (e != e_signs) {
+      // signs at the C2 positions 32(4q+i) + 16h + c
+      const uint16_t* s1 = a.sv1 + static_cast<size_t>(e) * 2 * I + 128 * q + c;
+      const uint16_t* s2 = a.su2 + static_cast<size_t>(e) * I + 128 * q + c;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sg[h][i] = h2f(s1[32 * i + 16 * h]);
-      su[h][i] = h2f(s1[I + 32 * i + 16 * h]);
-      sd[h][i] = h2f(s2[32 * i + 16 * h]);
+        for (int i = 0; i < 4; ++i) {
+          sg[h][i] = h2f(s1[32 * i + 16 * h]);
+          su[h][i] = h2f(s1[I + 32 * i + 16 * h]);
+          sd[h][i] = h2f(s2[32 * i + 16 * h]);
+        }
+      e_signs = e;
     }
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float gg = (g[h][i] * kScale) * sg[h][i];
-      const float uu = (u[h][i] * kScale) * su[h][i];
-      v[h][i] = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * uu * sd[h][i];   // SiLU(g) * u * su2
+      for (int i = 0; i < 4; ++i) {
+        const float gg = (g[h][i] * kScale) * sg[h][i];
+        const float uu = (u[h][i] * kScale) * su[h][i];
+        v[h][i] = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * uu * sd[h][i];   // SiLU(g) * u * su2
+      }
+    f4 y[2];
+    hmfma::from_c2(o, v, y);
+    _Float16* out = static_cast<_Float16*>(a.b) + static_cast<size_t>(p) * a.ldb + 32 * c + 4 * q;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const hmfma::half4v r = {static_cast<_Float16>(y[h][0] * kScale), static_cast<_Float16>(y[h][1] * kScale),
+                               static_cast<_Float16>(y[h][2] * kScale), static_cast<_Float16>(y[h][3] * kScale)};
+      *reinterpret_cast<hmfma::half4v*>(out + 16 * h) = r;
     }
-  f4 y[2];
-  hmfma::from_c2(o, v, y);
-  _Float16* out = static_cast<_Float16*>(a.b) + static_cast<size_t>(p) * a.ldb + 32 * c + 4 * q;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const hmfma::half4v r = {static_cast<_Float16>(y[h][0] * kScale), static_cast<_Float16>(y[h][1] * kScale),
-                      static_cast<_Float16>(y[h][2] * kScale), static_cast<_Float16>(y[h][3] * kScale)};
-    *reinterpret_cast<hmfma::half4v*>(out + 16 * h) = r;
+    if (en < 0) break;
+    p = pn;
+    e = en;
+    xg = ng;
+    xu = nu;
   }
 }
 
@@ -272,18 +296,18 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
     return;
   }
   const int lane = threadIdx.x & 63;
-  const int nseg = EPL > 0 ? 1 : row_segments(a.rot);
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if constexpr (EPL == 8 && !MX && SMAX == 0) {
+    if (!a.rot.identity) {                       // kActSlots slots per wavefront (launch_act)
+      if (item * kActSlots < a.routes) act_rows_mfma(a, item * kActSlots, lane);
+      return;
+    }
+  }
+  const int nseg = EPL > 0 ? 1 : row_segments(a.rot);
   const int p = item / nseg, seg = item - p * nseg;
   if (p >= a.routes) return;
   const int e = a.slot_expert[p];                // -1 past the filled slots (dropped routes)
   if (e < 0) return;
-  if constexpr (EPL == 8 && !MX && SMAX == 0) {
-    if (!a.rot.identity) {
-      act_row_mfma(a, p, e, lane);
-      return;
-    }
-  }
   ActBody<MX, SMAX> body{a, lane, p, e, a.rot.n, SMAX};
   run_segment<EPL>(a.rot, seg, body);
 }
@@ -705,7 +729,11 @@ int combine_waves(int hidden, int top_k) {
 
 void launch_act(const ActArgs& a_in, bool mx, hipStream_t s) {
   ActArgs a = a_in;
-  a.act_blocks = static_cast<int>(blocks_for(static_cast<long long>(a.routes) * row_segments(a.rot)));
+  // (rows of 512 values from one fp16 plane, rotated: kActSlots slots per wavefront, see k_act; a
+  // plane is launched as k_act<E, false, 0> whatever mx says)
+  const bool grouped = a.z16 && a.rot.pow2 && a.rot.n == 512 && !a.rot.identity;
+  a.act_blocks = grouped ? static_cast<int>(blocks_for((static_cast<long long>(a.routes) + kActSlots - 1) / kActSlots))
+                         : static_cast<int>(blocks_for(static_cast<long long>(a.routes) * row_segments(a.rot)));
   const long long zero_blocks = a.y_zero ? (a.y_count + 1023) / 1024 : 0;
   const unsigned grid = static_cast<unsigned>(a.act_blocks + zero_blocks);
   dispatch_epl(a.rot, [&](auto epl) {
