@@ -297,10 +297,14 @@ def test_w4a8_tiny():
     assert err <= TOL_W4A8_EMU
 
 
-def test_scales_and_signs_at_two_byte_alignment():
+@pytest.mark.parametrize("name,T,over,bound", [("decode", 16, {}, 2e-4),
+                                              ("tiny", 600, dict(hidden=1024, inter=512), 2.0 ** -10)])
+def test_scales_and_signs_at_two_byte_alignment(name, T, over, bound):
     """fp16 scale and sign vectors one element past a 16-byte boundary (the ABI asks only 2-byte
-    alignment): the row kernels take their strided loads instead of 16-byte ones, same result."""
-    c = Case("decode", 16)
+    alignment): the row kernels take their strided loads instead of 16-byte ones, same result.
+    T = 600 with H = 1024, I = 512: one fp16 plane per GEMM, so the rotations run on the matrix
+    cores and the combine reads its signs two bytes at a time."""
+    c = Case(name, T, **over)
     ref = c.run().clone()
     W = c.L.DeviceWeights
     shifted = []
@@ -315,10 +319,15 @@ def test_scales_and_signs_at_two_byte_alignment():
     c.weights = W(*shifted)
     y = c.run()
     err = rel_err(y.cpu().numpy(), c.oracle_w4a16)
-    say(f"[result] {c.label} shifted scales rel err {err:.3e}")
+    diff = float((y - ref).abs().max()) / float(ref.abs().max())
+    say(f"[result] {c.label} shifted scales rel err {err:.3e}, against the aligned run {diff:.3e}")
     assert err <= TOL_W4A16
-    # the two layouts run the butterfly stages in another order: fp32 rounding, and the odd fp16 step
-    assert torch.allclose(y, ref, rtol=0, atol=2e-4 * float(ref.abs().max()))
+    # The input rotation's two layouts run the butterfly stages in another order (fp32 rounding, the
+    # odd last-bit flip of an fp16 rotated input). With fp32 K-split planes that stays within 2e-4 of
+    # the output's maximum; with one fp16 plane per GEMM a flipped bit also passes through the fp16
+    # roundings of z, of the matrix-core rotation stages and of v, each able to move an output by one
+    # fp16 unit (2^-11) of its scale: two units.
+    assert diff <= bound
 
 
 @pytest.mark.parametrize("w4a8", [False, True])
