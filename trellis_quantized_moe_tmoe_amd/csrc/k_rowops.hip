@@ -312,6 +312,105 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
   run_segment<EPL>(a.rot, seg, body);
 }
 
+// Few slots with I = 512 and fp32 K-split planes: one workgroup of four wavefronts per slot, so the
+// chain of dependent instructions each wavefront runs is about a quarter of a whole-row wavefront's
+// (at small batches that chain, not the chip's throughput, sets the kernel's time). Wavefront w holds
+// elements 128 w + lane and 128 w + 64 + lane; with i = 128 w + j the rotation is H_4 (x) H_128: the
+// 128-point transform inside each wavefront (its butterflies, scale 1/sqrt(128)), then H_4 across
+// the four wavefronts through LDS, in ascending order of the source wavefront, times 1/2.
+template <int SMAX>
+__global__ __launch_bounds__(256) void k_act_split(ActArgs a) {
+  constexpr int I = 512;
+  __shared__ float xs[3][4][128];               // gate, up, then the product, per wavefront
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int p = blockIdx.x;                     // the grid is one workgroup per slot
+  const int e = a.slot_expert[p];               // -1 past the filled slots: the whole workgroup leaves
+  if (e < 0) return;
+  const bool rot = !a.rot.identity;
+  const int i0 = 128 * w + lane, i1 = i0 + 64;
+  const size_t plane = static_cast<size_t>(a.routes) * 2 * I;
+  const float* zr = a.z + static_cast<size_t>(p) * 2 * I;
+  float t[SMAX][4];
+#pragma unroll
+  for (int sp = 0; sp < SMAX; ++sp) {
+    t[sp][0] = zr[sp * plane + i0];
+    t[sp][1] = zr[sp * plane + i1];
+    t[sp][2] = zr[sp * plane + I + i0];
+    t[sp][3] = zr[sp * plane + I + i1];
+  }
+  const uint16_t* c1 = a.scale1 + static_cast<size_t>(e) * 2 * I;
+  const uint16_t* s1 = a.sv1 + static_cast<size_t>(e) * 2 * I;
+  const uint16_t* s2 = a.su2 + static_cast<size_t>(e) * I;
+  const float cg0 = h2f(c1[i0]), cg1 = h2f(c1[i1]), cu0 = h2f(c1[I + i0]), cu1 = h2f(c1[I + i1]);
+  const float sg0 = h2f(s1[i0]), sg1 = h2f(s1[i1]), su0 = h2f(s1[I + i0]), su1 = h2f(s1[I + i1]);
+  const float sd0 = h2f(s2[i0]), sd1 = h2f(s2[i1]);
+  float g[2] = {0.f, 0.f}, u[2] = {0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < SMAX; ++sp) {           // split planes in ascending order
+    g[0] += t[sp][0];
+    g[1] += t[sp][1];
+    u[0] += t[sp][2];
+    u[1] += t[sp][3];
+  }
+  g[0] *= cg0;
+  g[1] *= cg1;
+  u[0] *= cu0;
+  u[1] *= cu1;
+  // H_4 across the wavefronts: value j of wavefront w becomes (1/2) sum over v of (-1)^popcount(w & v)
+  // times value j of wavefront v
+  auto across = [&](int k, float (&v)[2]) {
+    xs[k][w][lane] = v[0];
+    xs[k][w][64 + lane] = v[1];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float acc = xs[k][0][64 * h + lane];
+#pragma unroll
+      for (int src = 1; src < 4; ++src) {
+        const float x = xs[k][src][64 * h + lane];
+        acc = (__builtin_popcount(w & src) & 1) ? acc - x : acc + x;
+      }
+      v[h] = 0.5f * acc;
+    }
+  };
+  if (rot) {
+    fwht_segment<2>(g, lane);
+    fwht_segment<2>(u, lane);
+    // gate and up cross in one exchange (one barrier)
+    xs[0][w][lane] = g[0];
+    xs[0][w][64 + lane] = g[1];
+    xs[1][w][lane] = u[0];
+    xs[1][w][64 + lane] = u[1];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float ag = xs[0][0][64 * h + lane], au = xs[1][0][64 * h + lane];
+#pragma unroll
+      for (int src = 1; src < 4; ++src) {
+        const float xg = xs[0][src][64 * h + lane], xu = xs[1][src][64 * h + lane];
+        const bool neg = __builtin_popcount(w & src) & 1;
+        ag = neg ? ag - xg : ag + xg;
+        au = neg ? au - xu : au + xu;
+      }
+      g[h] = 0.5f * ag;
+      u[h] = 0.5f * au;
+    }
+  }
+  float b[2];
+  {
+    const float gg0 = g[0] * sg0, uu0 = u[0] * su0, gg1 = g[1] * sg1, uu1 = u[1] * su1;
+    b[0] = gg0 * __builtin_amdgcn_rcpf(1.0f + __expf(-gg0)) * uu0 * sd0;   // SiLU(g) * u * su2
+    b[1] = gg1 * __builtin_amdgcn_rcpf(1.0f + __expf(-gg1)) * uu1 * sd1;
+  }
+  if (rot) {
+    fwht_segment<2>(b, lane);
+    across(2, b);
+  }
+  _Float16* out = static_cast<_Float16*>(a.b) + static_cast<size_t>(p) * a.ldb;
+  out[i0] = static_cast<_Float16>(b[0]);
+  out[i1] = static_cast<_Float16>(b[1]);
+}
+
 // Rotates one route's row held in LDS in place: o = wt * sv2_e * R_H(row).
 struct CombineRotBody {
   const CombineArgs& a;
@@ -714,6 +813,7 @@ void dispatch_smax(int most, F&& f) {
 }
 
 constexpr size_t kCombineLdsBytes = 65536;
+constexpr int kActSplitMaxSlots = 2048;   // slots up to which the activation takes a workgroup per slot
 
 // Wavefronts per combine workgroup: at most 16, at most top_k, and LDS within kCombineLdsBytes
 // (which keeps H = 4096 at 3, inside that kernel's 256-thread bound).
@@ -736,6 +836,14 @@ void launch_act(const ActArgs& a_in, bool mx, hipStream_t s) {
                          : static_cast<int>(blocks_for(static_cast<long long>(a.routes) * row_segments(a.rot)));
   const long long zero_blocks = a.y_zero ? (a.y_count + 1023) / 1024 : 0;
   const unsigned grid = static_cast<unsigned>(a.act_blocks + zero_blocks);
+  // few slots of 512 values from fp32 planes (fp16 operands, y not zeroed here): a workgroup per slot
+  if (!mx && !a.z16 && a.rot.pow2 && a.rot.n == 512 && !a.y_zero && a.routes <= kActSplitMaxSlots) {
+    dispatch_smax(a.nsplit, [&](auto sm) {
+      constexpr int SM = decltype(sm)::value;
+      if constexpr (SM > 0) hipLaunchKernelGGL((k_act_split<SM>), dim3(a.routes), dim3(256), 0, s, a);
+    });
+    return;
+  }
   dispatch_epl(a.rot, [&](auto epl) {
     dispatch_smax(a.z16 ? 0 : a.nsplit, [&](auto sm) {
       constexpr int E = decltype(epl)::value, SM = decltype(sm)::value;
