@@ -317,8 +317,10 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
 // (at small batches that chain, not the chip's throughput, sets the kernel's time). Wavefront w holds
 // elements 128 w + lane and 128 w + 64 + lane; with i = 128 w + j the rotation is H_4 (x) H_128: the
 // 128-point transform inside each wavefront (its butterflies, scale 1/sqrt(128)), then H_4 across
-// the four wavefronts through LDS, in ascending order of the source wavefront, times 1/2.
-template <int SMAX>
+// the four wavefronts through LDS, in ascending order of the source wavefront, times 1/2. MX: the
+// product goes out as MXFP8; each 32-lane half of a wavefront holds 32 consecutive elements, one
+// E8M0 block.
+template <bool MX, int SMAX>
 __global__ __launch_bounds__(256) void k_act_split(ActArgs a) {
   constexpr int I = 512;
   __shared__ float xs[3][4][128];               // gate, up, then the product, per wavefront
@@ -406,9 +408,16 @@ __global__ __launch_bounds__(256) void k_act_split(ActArgs a) {
     fwht_segment<2>(b, lane);
     across(2, b);
   }
-  _Float16* out = static_cast<_Float16*>(a.b) + static_cast<size_t>(p) * a.ldb;
-  out[i0] = static_cast<_Float16>(b[0]);
-  out[i1] = static_cast<_Float16>(b[1]);
+  if constexpr (MX) {
+    uint8_t* q = static_cast<uint8_t*>(a.b) + static_cast<size_t>(p) * I;
+    uint8_t* sc = a.b_scale + static_cast<size_t>(p) * (I / 32);
+    mx_store(b[0], lane, q, sc, i0);
+    mx_store(b[1], lane, q, sc, i1);
+  } else {
+    _Float16* out = static_cast<_Float16*>(a.b) + static_cast<size_t>(p) * a.ldb;
+    out[i0] = static_cast<_Float16>(b[0]);
+    out[i1] = static_cast<_Float16>(b[1]);
+  }
 }
 
 // Rotates one route's row held in LDS in place: o = wt * sv2_e * R_H(row).
@@ -836,11 +845,14 @@ void launch_act(const ActArgs& a_in, bool mx, hipStream_t s) {
                          : static_cast<int>(blocks_for(static_cast<long long>(a.routes) * row_segments(a.rot)));
   const long long zero_blocks = a.y_zero ? (a.y_count + 1023) / 1024 : 0;
   const unsigned grid = static_cast<unsigned>(a.act_blocks + zero_blocks);
-  // few slots of 512 values from fp32 planes (fp16 operands, y not zeroed here): a workgroup per slot
-  if (!mx && !a.z16 && a.rot.pow2 && a.rot.n == 512 && !a.y_zero && a.routes <= kActSplitMaxSlots) {
+  // few slots of 512 values from fp32 planes (y not zeroed here): a workgroup per slot
+  if (!a.z16 && a.rot.pow2 && a.rot.n == 512 && !a.y_zero && a.routes <= kActSplitMaxSlots) {
     dispatch_smax(a.nsplit, [&](auto sm) {
       constexpr int SM = decltype(sm)::value;
-      if constexpr (SM > 0) hipLaunchKernelGGL((k_act_split<SM>), dim3(a.routes), dim3(256), 0, s, a);
+      if constexpr (SM > 0) {
+        if (mx) hipLaunchKernelGGL((k_act_split<true, SM>), dim3(a.routes), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_act_split<false, SM>), dim3(a.routes), dim3(256), 0, s, a);
+      }
     });
     return;
   }
