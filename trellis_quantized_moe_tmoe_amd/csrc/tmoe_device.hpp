@@ -334,11 +334,16 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return e > 127 ? 127 : e;
 }
 
-// Maximum of |v| over the 32-lane half of the wavefront this lane belongs to.
+// Maximum of |v| over the 32-lane half of the wavefront this lane belongs to: a butterfly over the
+// lane bits 0-4 by DPP and swizzle exchanges (the rotation by 8 inside a 16-lane row pairs the two
+// 8-lane groups as an exchange of bit 3 would); max is exact, so the order does not matter.
 __device__ __forceinline__ float half_wave_amax(float v) {
   float a = fabsf(v);
-#pragma unroll
-  for (int s = 1; s < 32; s <<= 1) a = fmaxf(a, __shfl_xor(a, s, 64));
+  a = fmaxf(a, lane_partner<1>(a));
+  a = fmaxf(a, lane_partner<2>(a));
+  a = fmaxf(a, lane_partner<4>(a));
+  a = fmaxf(a, lane_partner<8>(a));
+  a = fmaxf(a, lane_partner<16>(a));
   return a;
 }
 
