@@ -52,8 +52,9 @@ __device__ __forceinline__ void mx_store(float v, int lane, uint8_t* q_row, uint
 // Input rotation of one route (token t, expert e): a = R_H(su1_e * x_t) into operand row p.
 // The butterflies of fwht_segment act on every bit of the element index, so the transform is the
 // same whether a lane holds elements off + 64 i + lane (strided) or off + S lane + i (blocked); the
-// fp16 path with 8 or more values per lane uses the blocked layout, whose loads and stores are 16
-// bytes wide (MXFP8 keeps the strided one: its 32-value blocks are half-wavefronts there).
+// fp16 path with 8 or more values per lane and the MXFP8 path with 8 or 16 use the blocked layout,
+// whose loads and stores are 8 or 16 bytes wide (other MXFP8 rows keep the strided one, where a
+// 32-value block is a half-wavefront).
 template <bool MX>
 struct RotateBody {
   const RotateArgs& a;
@@ -62,6 +63,12 @@ struct RotateBody {
   __device__ __forceinline__ void run(int off) {
     float v[S];
     // (the signs need only 2-byte alignment by contract; x and the arena are 16-byte aligned)
+    if constexpr (MX && (S == 8 || S == 16)) {
+      if ((reinterpret_cast<uintptr_t>(a.su1) & 15) == 0) {
+        run_mx_blocked<S>(off);
+        return;
+      }
+    }
     if constexpr (!MX && S >= 8) {
       if ((reinterpret_cast<uintptr_t>(a.su1) & 15) == 0) {
         typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
@@ -91,6 +98,42 @@ struct RotateBody {
 #pragma unroll
     for (int i = 0; i < S; ++i) v[i] = bf16_to_f32(xr[64 * i]) * h2f(sr[64 * i]);
     finish<S>(v, off);
+  }
+  // MXFP8 in the blocked layout (element off + S lane + i in v[i]): a 32-value block is 32 / S
+  // adjacent lanes, so its maximum is the lane's own S values and one (S = 16) or two (S = 8) lane
+  // exchanges, and the lane writes its S codes with one 16- or 8-byte store.
+  template <int S>
+  __device__ __forceinline__ void run_mx_blocked(int off) {
+    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+    float v[S];
+    const u16x8* xr = reinterpret_cast<const u16x8*>(a.x + static_cast<size_t>(t) * H + off + S * lane);
+    const u16x8* sr = reinterpret_cast<const u16x8*>(a.su1 + static_cast<size_t>(e) * H + off + S * lane);
+#pragma unroll
+    for (int c = 0; c < S / 8; ++c) {
+      const u16x8 xv = xr[c], sv = sr[c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[8 * c + i] = bf16_to_f32(xv[i]) * h2f(sv[i]);
+    }
+    if (!a.rot.identity) fwht_segment<S>(v, lane);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < S; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, lane_partner<1>(m));
+    if constexpr (S == 8) m = fmaxf(m, lane_partner<2>(m));
+    const int ex = mx_exponent(m);
+    uint32_t w[S / 4];
+#pragma unroll
+    for (int k = 0; k < S / 4; ++k) {
+      float q4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q4[j] = fminf(fmaxf(ldexpf(v[4 * k + j], -ex), -448.0f), 448.0f);
+      w[k] = fp8x2_from_f32(q4[0], q4[1]) | (fp8x2_from_f32(q4[2], q4[3]) << 16);
+    }
+    uint8_t* q = static_cast<uint8_t*>(a.a1) + static_cast<size_t>(p) * H + off + S * lane;
+    if constexpr (S == 16) *reinterpret_cast<uint4*>(q) = make_uint4(w[0], w[1], w[2], w[3]);
+    else *reinterpret_cast<uint2*>(q) = make_uint2(w[0], w[1]);
+    if ((lane & (32 / S - 1)) == 0)
+      a.a1_scale[static_cast<size_t>(p) * (H / 32) + ((off + S * lane) >> 5)] = static_cast<uint8_t>(ex + 127);
   }
   // NB consecutive 128-blocks from element off: every block's loads are issued before the first
   // block is rotated (a long non-power-of-two row would otherwise wait on each block in turn).
